@@ -1,0 +1,215 @@
+// C ABI of the attention-with-sinks library: argument checks, workspace carve-up,
+// kernel launches and the opt-in per-kernel timing records.  The operations are
+// defined in include/attn_sink.h.
+#include "../../include/attn_sink.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <mutex>
+#include <vector>
+
+#include "kernels.h"
+
+namespace attn_sink {
+
+const char* kernel_name(int id) {
+  switch (id) {
+    case K_FWD: return "attn_sink_fwd_kernel";
+    case K_BWD_PRE: return "attn_sink_bwd_pre_kernel";
+    case K_BWD_DKDV: return "attn_sink_bwd_dkdv_kernel";
+    case K_BWD_FINISH: return "attn_sink_bwd_finish_kernel";
+    default: return "?";
+  }
+}
+
+namespace {
+
+// ---- opt-in timing records
+struct Record {
+  int kernel;
+  hipEvent_t start, stop;
+};
+std::mutex g_mu;
+bool g_timing = false;
+std::vector<Record> g_records;
+
+void clear_records_locked() {
+  for (auto& r : g_records) {
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  g_records.clear();
+}
+
+template <typename F>
+attn_sink_status timed_launch(int kernel, hipStream_t stream, F&& launch) {
+  bool timing;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    timing = g_timing;
+  }
+  Record rec{kernel, nullptr, nullptr};
+  if (timing) {
+    if (hipEventCreate(&rec.start) != hipSuccess || hipEventCreate(&rec.stop) != hipSuccess) return ATTN_SINK_ERR_HIP;
+    if (hipEventRecord(rec.start, stream) != hipSuccess) return ATTN_SINK_ERR_HIP;
+  }
+  hipError_t e = launch();
+  if (e != hipSuccess) return ATTN_SINK_ERR_HIP;
+  if (timing) {
+    if (hipEventRecord(rec.stop, stream) != hipSuccess) return ATTN_SINK_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_records.push_back(rec);
+  }
+  return ATTN_SINK_OK;
+}
+
+attn_sink_status check_shape(const attn_sink_shape* s) {
+  if (!s) return ATTN_SINK_ERR_INVALID_ARG;
+  if (s->dtype != ATTN_SINK_BF16 && s->dtype != ATTN_SINK_FP32) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (s->head_dim != kHeadDimBuilt) return s->head_dim > 0 ? ATTN_SINK_ERR_UNSUPPORTED : ATTN_SINK_ERR_INVALID_ARG;
+  if (s->num_heads_q < 1 || s->num_heads_kv < 1 || s->num_heads_q % s->num_heads_kv != 0)
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (s->num_seqs < 1 || s->total_q < 0 || s->total_k < 0 || s->max_seqlen_q < 0 || s->max_seqlen_k < 0)
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (!s->cu_seqlens_q || !s->cu_seqlens_k) return ATTN_SINK_ERR_INVALID_ARG;
+  if (!(s->softmax_scale > 0.f) || !std::isfinite(s->softmax_scale)) return ATTN_SINK_ERR_INVALID_ARG;
+  if (s->causal != 0 && s->causal != 1) return ATTN_SINK_ERR_INVALID_ARG;
+  // grid limits: y is the tile index (<= 65535); x is heads * sequences
+  if ((long long)s->num_heads_q * s->num_seqs > 0x7fffffffLL) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (s->max_seqlen_q > 65535LL * 128 || s->max_seqlen_k > 65535LL * 128) return ATTN_SINK_ERR_UNSUPPORTED;
+  // 32-bit row indices inside the kernels
+  if ((long long)s->total_q * s->num_heads_q * kHeadDimBuilt > 0x7fffffffLL * 4LL) return ATTN_SINK_ERR_UNSUPPORTED;
+  return ATTN_SINK_OK;
+}
+
+FwdArgs fwd_args(const attn_sink_shape* s, const void* q, const void* k, const void* v, const float* sinks,
+                 const void* o, const float* lse) {
+  FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.sinks = sinks;
+  a.o = const_cast<void*>(o);
+  a.lse = const_cast<float*>(lse);
+  a.cu_q = s->cu_seqlens_q;
+  a.cu_k = s->cu_seqlens_k;
+  a.hq = s->num_heads_q;
+  a.hkv = s->num_heads_kv;
+  a.num_seqs = s->num_seqs;
+  a.total_q = s->total_q;
+  a.total_k = s->total_k;
+  a.max_q = s->max_seqlen_q;
+  a.max_k = s->max_seqlen_k;
+  a.scale = s->softmax_scale;
+  a.causal = s->causal;
+  a.window = s->window > 0 ? s->window : 0;
+  return a;
+}
+
+}  // namespace
+}  // namespace attn_sink
+
+using namespace attn_sink;
+
+extern "C" {
+
+attn_sink_status attn_sink_fwd(const attn_sink_shape* shape, const void* q, const void* k, const void* v,
+                               const float* sinks, void* o, float* lse, hipStream_t stream) {
+  attn_sink_status st = check_shape(shape);
+  if (st != ATTN_SINK_OK) return st;
+  const bool any_q = shape->total_q > 0, any_k = shape->total_k > 0;
+  if (!sinks || (any_q && (!q || !o || !lse)) || (any_k && (!k || !v))) return ATTN_SINK_ERR_INVALID_ARG;
+  if (!any_q) return ATTN_SINK_OK;
+  FwdArgs a = fwd_args(shape, q, k, v, sinks, o, lse);
+  const int fp32 = shape->dtype == ATTN_SINK_FP32;
+  return timed_launch(K_FWD, stream, [&] { return launch_fwd(a, fp32, stream); });
+}
+
+size_t attn_sink_bwd_workspace_bytes(const attn_sink_shape* shape) {
+  if (check_shape(shape) != ATTN_SINK_OK) return 0;
+  return bwd_workspace_layout(shape->num_heads_q, shape->num_heads_kv, shape->total_q, shape->total_k).total;
+}
+
+attn_sink_status attn_sink_bwd(const attn_sink_shape* shape, const void* q, const void* k, const void* v,
+                               const float* sinks, const void* o, const float* lse, const void* dout, void* dq,
+                               void* dk, void* dv, float* dsinks, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  attn_sink_status st = check_shape(shape);
+  if (st != ATTN_SINK_OK) return st;
+  const bool any_q = shape->total_q > 0, any_k = shape->total_k > 0;
+  if (!sinks || !dsinks) return ATTN_SINK_ERR_INVALID_ARG;
+  if (any_q && (!q || !o || !lse || !dout || !dq)) return ATTN_SINK_ERR_INVALID_ARG;
+  if (any_k && (!k || !v || !dk || !dv)) return ATTN_SINK_ERR_INVALID_ARG;
+  const BwdWorkspace ws = bwd_workspace_layout(shape->num_heads_q, shape->num_heads_kv, shape->total_q, shape->total_k);
+  if (!workspace || workspace_bytes < ws.total || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return ATTN_SINK_ERR_WORKSPACE;
+
+  BwdArgs a;
+  a.f = fwd_args(shape, q, k, v, sinks, o, lse);
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dsinks = dsinks;
+  char* base = static_cast<char*>(workspace);
+  a.dq_acc = reinterpret_cast<float*>(base + ws.dq_acc);
+  a.dk_acc = reinterpret_cast<float*>(base + ws.dk_acc);
+  a.dv_acc = reinterpret_cast<float*>(base + ws.dv_acc);
+  a.delta = reinterpret_cast<float*>(base + ws.delta);
+  a.dsink_part = reinterpret_cast<float*>(base + ws.dsink_part);
+  a.pre_blocks = ws.pre_blocks;
+  const int fp32 = shape->dtype == ATTN_SINK_FP32;
+
+  st = timed_launch(K_BWD_PRE, stream, [&] { return launch_bwd_pre(a, fp32, stream); });
+  if (st != ATTN_SINK_OK) return st;
+  if (any_q && any_k) {
+    st = timed_launch(K_BWD_DKDV, stream, [&] { return launch_bwd_dkdv(a, fp32, stream); });
+    if (st != ATTN_SINK_OK) return st;
+  }
+  return timed_launch(K_BWD_FINISH, stream, [&] { return launch_bwd_finish(a, fp32, stream); });
+}
+
+const char* attn_sink_status_string(attn_sink_status status) {
+  switch (status) {
+    case ATTN_SINK_OK: return "ok";
+    case ATTN_SINK_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_SINK_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_SINK_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case ATTN_SINK_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+attn_sink_status attn_sink_timing_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (enable) clear_records_locked();
+  g_timing = enable != 0;
+  return ATTN_SINK_OK;
+}
+
+int attn_sink_timing_read(const char** names, int* launches, double* total_ms, int max) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  int cnt[K_COUNT] = {0};
+  double ms[K_COUNT] = {0};
+  for (auto& r : g_records) {
+    if (hipEventSynchronize(r.stop) != hipSuccess) return -1;
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, r.start, r.stop) != hipSuccess) return -1;
+    cnt[r.kernel] += 1;
+    ms[r.kernel] += t;
+  }
+  int n = 0;
+  for (int k = 0; k < K_COUNT; ++k) {
+    if (cnt[k] == 0) continue;
+    if (n < max) {
+      if (names) names[n] = kernel_name(k);
+      if (launches) launches[n] = cnt[k];
+      if (total_ms) total_ms[n] = ms[k];
+    }
+    ++n;
+  }
+  return n;
+}
+
+}  // extern "C"

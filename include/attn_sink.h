@@ -1,0 +1,142 @@
+/*
+ * attn_sink.h - C ABI of the MI355X (gfx950) attention-with-learnable-sinks library.
+ *
+ * What is computed.  For every sequence b of a packed batch and every query
+ * head h (kv head g = h / (Hq / Hkv)):
+ *
+ *   s_ij     = softmax_scale * <q_i, k_j>                     for visible keys j
+ *   P_ij     = exp(s_ij) / (sum_j' exp(s_ij') + exp(S_h))
+ *   P_sink_i = exp(S_h)  / (same denominator)
+ *   o_i      = sum_j P_ij v_j                  (the sink is never multiplied by V)
+ *   lse_i    = log(sum_j exp(s_ij) + exp(S_h))  (natural log, the sink included)
+ *
+ * This is the sink softmax of "Unlocking Agentic RL Training for GPT-OSS"
+ * (euno.news, zh), section on attention-sink support in FlashAttention V3:
+ * sub-section 带汇聚的注意力 (one learnable logit S_h per head appended to every
+ * score row as a virtual key, dropped before the product with V) and
+ * sub-section 数学公式 (the two probability formulas above).  The backward
+ * returns dq, dk, dv and the sink gradient of sub-section 反向传播,
+ * dS_h = -sum_i P_sink_i * D_i with D_i = <dO_i, o_i>.
+ *
+ * Visibility (masks are not on the pages; this ABI defines them): key j of a
+ * sequence with n_q queries and n_k keys is visible to query i when
+ *   (causal == 0 || j <= i + n_k - n_q) && (window <= 0 || j > i + n_k - n_q - window).
+ * "window = W" therefore means W keys including the diagonal.  The sink is
+ * visible to every row.
+ *
+ * Layouts (all contiguous, row-major, element type given by dtype):
+ *   q, o, dout, dq : [total_q, Hq,  head_dim]
+ *   k, v, dk, dv   : [total_k, Hkv, head_dim]
+ *   lse            : [Hq, total_q] float32, natural log, includes the sink
+ *   sinks, dsinks  : [Hq] float32, in score units (not multiplied by softmax_scale)
+ *   cu_seqlens_q/k : [num_seqs + 1] int32, DEVICE memory, cu[0] = 0, nondecreasing,
+ *                    cu[num_seqs] = total.  Fixed-length batches use [0, N, 2N, ...].
+ *
+ * Ownership: the caller allocates every buffer (device memory for all tensors,
+ * including the backward workspace).  The library allocates no device memory,
+ * keeps no state between calls (apart from the opt-in timing records below),
+ * never synchronises the stream, and enqueues all work on `stream` in order.
+ * Outputs (o, lse, dq, dk, dv, dsinks) are overwritten, not accumulated.
+ *
+ * Errors: every argument check runs on the host before anything is enqueued, so
+ * on any non-OK status nothing has been enqueued.  ATTN_SINK_ERR_HIP reports a
+ * launch error taken from the HIP runtime.  Faults inside a kernel are
+ * asynchronous and surface at the caller's next synchronisation.  The kernels
+ * clamp cu_seqlens entries to [0, total] before use, so a malformed cu_seqlens
+ * gives wrong numbers but no out-of-bounds access; sequences longer than
+ * max_seqlen_* are only partly computed (caller contract: max_seqlen_* >= every
+ * sequence length).
+ *
+ * Thread safety: calls are reentrant; concurrent calls on different streams are
+ * independent (they must not share output or workspace buffers).
+ */
+#ifndef ATTN_SINK_H
+#define ATTN_SINK_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_SINK_OK = 0,
+  ATTN_SINK_ERR_INVALID_ARG = 1,  /* null pointer, bad count, Hq % Hkv != 0, ... */
+  ATTN_SINK_ERR_UNSUPPORTED = 2,  /* well-formed but not built: head_dim != 64, dtype */
+  ATTN_SINK_ERR_WORKSPACE = 3,    /* backward workspace missing or smaller than required */
+  ATTN_SINK_ERR_HIP = 4           /* the HIP runtime refused a launch */
+} attn_sink_status;
+
+typedef enum {
+  ATTN_SINK_BF16 = 0,  /* q, k, v, o, dout, dq, dk, dv in bfloat16; MFMA bf16 x bf16 -> fp32 */
+  ATTN_SINK_FP32 = 1   /* the same tensors in float32; MFMA fp32 x fp32 -> fp32 */
+} attn_sink_dtype;
+
+typedef struct {
+  int dtype;               /* attn_sink_dtype */
+  int head_dim;            /* must be 64 */
+  int num_heads_q;         /* Hq  >= 1 */
+  int num_heads_kv;        /* Hkv >= 1, Hq % Hkv == 0 (GQA: heads h of one kv head are contiguous) */
+  int num_seqs;            /* >= 1 */
+  int total_q;             /* rows of q / o (>= 0) */
+  int total_k;             /* rows of k / v (>= 0) */
+  int max_seqlen_q;        /* >= every query length; sizes the launch grid */
+  int max_seqlen_k;        /* >= every key length */
+  const int* cu_seqlens_q; /* device, [num_seqs + 1] */
+  const int* cu_seqlens_k; /* device, [num_seqs + 1] */
+  float softmax_scale;     /* multiplies q.k (e.g. 1/sqrt(head_dim)); finite, > 0 */
+  int causal;              /* 0 or 1 */
+  int window;              /* <= 0: none; else W keys including the diagonal */
+} attn_sink_shape;
+
+/* Forward (sub-sections 带汇聚的注意力 and 数学公式 of the page cited above).
+ * Writes o (dtype) and lse (float32).  sinks may hold -INFINITY (then the head
+ * is standard attention); a row that sees no key and has S_h = -inf gets
+ * o = 0 and lse = -inf.  +INFINITY sinks are outside the domain. */
+attn_sink_status attn_sink_fwd(const attn_sink_shape* shape,
+                               const void* q, const void* k, const void* v,
+                               const float* sinks,
+                               void* o, float* lse,
+                               hipStream_t stream);
+
+/* Bytes of device workspace attn_sink_bwd needs for `shape` (0 on invalid shape). */
+size_t attn_sink_bwd_workspace_bytes(const attn_sink_shape* shape);
+
+/* Backward of attn_sink_fwd for upstream gradient dout (sub-section 反向传播 of
+ * the page cited above for dsinks; dq, dk, dv by the chain rule through the
+ * softmax over the score row with the sink column appended).
+ * o and lse must be the forward's outputs for the same inputs.  Writes dq (dtype,
+ * layout of q), dk/dv (dtype, layout of k) and dsinks (float32, [Hq]).
+ * workspace: device memory of at least attn_sink_bwd_workspace_bytes(shape)
+ * bytes, 256-byte aligned, owned by the caller, contents need not be initialised
+ * and are garbage afterwards.  dk, dv and dq are accumulated with floating-point
+ * atomics in the workspace, so their last bits can differ between runs; dsinks
+ * is reduced in a fixed order and is bitwise reproducible. */
+attn_sink_status attn_sink_bwd(const attn_sink_shape* shape,
+                               const void* q, const void* k, const void* v,
+                               const float* sinks,
+                               const void* o, const float* lse, const void* dout,
+                               void* dq, void* dk, void* dv, float* dsinks,
+                               void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* Static, human-readable name of a status code. */
+const char* attn_sink_status_string(attn_sink_status status);
+
+/* Opt-in per-kernel timing for measurement harnesses.  While enabled, every
+ * kernel the two entry points launch is bracketed by HIP events on the launch
+ * stream (this adds event records to the stream, nothing else).
+ * attn_sink_timing_enable(1) clears earlier records; (0) stops recording.
+ * attn_sink_timing_read synchronises on the recorded events and fills, for up to
+ * `max` kernels, the kernel name, the number of launches and the summed duration
+ * in milliseconds; it returns the number of distinct kernels (or -1 on error).
+ * Names point to static strings.  Not thread-safe: one harness at a time. */
+attn_sink_status attn_sink_timing_enable(int enable);
+int attn_sink_timing_read(const char** names, int* launches, double* total_ms, int max);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_SINK_H */

@@ -1,0 +1,138 @@
+"""Host-only checks of the C ABI: the library loads, exports what the header
+declares, and rejects bad arguments before anything reaches a GPU."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import attention_learnable_sinks_amd as als
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_sink.h")
+FAKE = 0x100000  # never dereferenced: every case below fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return als.load()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_sink_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == sorted(["attn_sink_fwd", "attn_sink_bwd", "attn_sink_bwd_workspace_bytes",
+                                  "attn_sink_status_string", "attn_sink_timing_enable", "attn_sink_timing_read"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", als.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (attn_sink_\w+)", out))
+    for name in _declared():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings(lib):
+    for st in range(5):
+        assert lib.attn_sink_status_string(st)
+    assert lib.attn_sink_status_string(0) == b"ok"
+    assert lib.attn_sink_status_string(99) == b"unknown status"
+
+
+def _shape(**kw):
+    base = dict(dtype=als.BF16, head_dim=64, num_heads_q=8, num_heads_kv=2, num_seqs=1, total_q=128,
+                total_k=128, max_seqlen_q=128, max_seqlen_k=128, cu_seqlens_q=FAKE, cu_seqlens_k=FAKE,
+                softmax_scale=0.125, causal=1, window=0)
+    base.update(kw)
+    return als.Shape(**base)
+
+
+BAD_SHAPES = [
+    (dict(head_dim=128), als.ERR_UNSUPPORTED),
+    (dict(head_dim=0), als.ERR_INVALID_ARG),
+    (dict(dtype=7), als.ERR_UNSUPPORTED),
+    (dict(num_heads_q=6, num_heads_kv=4), als.ERR_INVALID_ARG),
+    (dict(num_heads_kv=0), als.ERR_INVALID_ARG),
+    (dict(num_seqs=0), als.ERR_INVALID_ARG),
+    (dict(num_seqs=-3), als.ERR_INVALID_ARG),
+    (dict(total_q=-1), als.ERR_INVALID_ARG),
+    (dict(max_seqlen_k=-1), als.ERR_INVALID_ARG),
+    (dict(cu_seqlens_q=None), als.ERR_INVALID_ARG),
+    (dict(cu_seqlens_k=None), als.ERR_INVALID_ARG),
+    (dict(softmax_scale=0.0), als.ERR_INVALID_ARG),
+    (dict(softmax_scale=float("nan")), als.ERR_INVALID_ARG),
+    (dict(softmax_scale=float("inf")), als.ERR_INVALID_ARG),
+    (dict(causal=2), als.ERR_INVALID_ARG),
+    (dict(max_seqlen_q=65535 * 128 + 1), als.ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_SHAPES, ids=[str(k) for k, _ in BAD_SHAPES])
+def test_fwd_rejects_bad_shape(lib, kw, status):
+    s = _shape(**kw)
+    assert lib.attn_sink_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == status
+
+
+@pytest.mark.parametrize("kw,status", BAD_SHAPES, ids=[str(k) for k, _ in BAD_SHAPES])
+def test_bwd_rejects_bad_shape(lib, kw, status):
+    s = _shape(**kw)
+    args = [FAKE] * 11 + [FAKE, 1 << 40, None]
+    assert lib.attn_sink_bwd(ctypes.byref(s), *args) == status
+    assert lib.attn_sink_bwd_workspace_bytes(ctypes.byref(s)) == 0
+
+
+def test_null_shape(lib):
+    assert lib.attn_sink_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == als.ERR_INVALID_ARG
+    assert lib.attn_sink_bwd_workspace_bytes(None) == 0
+
+
+@pytest.mark.parametrize("slot", range(6))
+def test_fwd_rejects_null_tensor(lib, slot):
+    ptrs = [FAKE] * 6
+    ptrs[slot] = None
+    s = _shape()
+    assert lib.attn_sink_fwd(ctypes.byref(s), *ptrs, None) == als.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("slot", range(11))
+def test_bwd_rejects_null_tensor(lib, slot):
+    ptrs = [FAKE] * 11
+    ptrs[slot] = None
+    s = _shape()
+    assert lib.attn_sink_bwd(ctypes.byref(s), *ptrs, FAKE, 1 << 40, None) == als.ERR_INVALID_ARG
+
+
+def test_workspace_size_formula(lib):
+    s = _shape(num_heads_q=64, num_heads_kv=8, total_q=4096, total_k=4096, max_seqlen_q=4096, max_seqlen_k=4096)
+    n = lib.attn_sink_bwd_workspace_bytes(ctypes.byref(s))
+    t, hq, hkv, d = 4096, 64, 8, 64
+    expect = t * hq * d * 4 + 2 * t * hkv * d * 4 + hq * t * 4 + hq * (t // 64) * 4
+    assert expect <= n <= expect + 5 * 256
+
+
+def test_bwd_rejects_small_or_misaligned_workspace(lib):
+    s = _shape()
+    need = lib.attn_sink_bwd_workspace_bytes(ctypes.byref(s))
+    assert need > 0
+    args = [FAKE] * 11
+    assert lib.attn_sink_bwd(ctypes.byref(s), *args, FAKE, need - 1, None) == als.ERR_WORKSPACE
+    assert lib.attn_sink_bwd(ctypes.byref(s), *args, None, need, None) == als.ERR_WORKSPACE
+    assert lib.attn_sink_bwd(ctypes.byref(s), *args, FAKE + 4, need, None) == als.ERR_WORKSPACE
+
+
+def test_timing_read_without_records(lib):
+    assert lib.attn_sink_timing_enable(1) == 0
+    assert lib.attn_sink_timing_read(None, None, None, 0) == 0
+    assert lib.attn_sink_timing_enable(0) == 0
+
+
+def test_load_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="not found"):
+        als.load(str(tmp_path / "missing.so"))

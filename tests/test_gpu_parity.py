@@ -1,0 +1,267 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Small cases compare every output element; they span several query and key
+tiles (forward tiles of 128 queries x 64 keys, backward tiles of 64 queries x
+128 keys) and end in ragged tails.  The five workload configurations run at
+full size in the launch configuration the benchmark times; there the oracle
+computes a sample (a kv group, or one head on sampled rows and keys) that it
+evaluates exactly.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import WORKLOADS, make_inputs, random_case
+from _parity import TOL, compare, gpu_fwd_bwd, oracle_bwd, to_dev
+
+pytestmark = pytest.mark.gpu
+ALL = ("o", "lse", "dq", "dk", "dv", "dsinks")
+
+
+def _full_case(als, inp, label, tol=None):
+    tol = TOL["bf16" if inp["q"].dtype == torch.bfloat16 else "fp32"] if tol is None else tol
+    print(f"[case] {label}", flush=True)
+    gpu = gpu_fwd_bwd(als, inp)
+    ref = oracle_bwd(inp)
+    return compare(gpu, ref, ALL, tol, label)
+
+
+# ----------------------------------------------------------------------------- small, every element
+def test_tiny_fp32(gpu_lib):
+    inp = make_inputs(WORKLOADS["tiny"])
+    _full_case(gpu_lib, inp, "tiny fp32")
+
+
+SMALL = [
+    # seqlens, hq, hkv, causal, window, sink distribution
+    ([300], 8, 2, True, 0, ("normal",)),
+    ([1, 77, 300, 0, 129], 4, 1, True, 0, ("normal",)),
+    ([333, 64, 200], 8, 8, True, 37, ("uniform", -2.0, 4.0)),
+    ([257], 4, 2, False, 0, ("normal",)),
+    ([190, 450], 4, 4, False, 100, ("uniform", -2.0, 8.0)),
+    ([513], 16, 2, True, 128, ("normal",)),
+]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("case", SMALL, ids=[f"{c[0]}-{c[1]}x{c[2]}-c{int(c[3])}-w{c[4]}" for c in SMALL])
+def test_small_ragged(gpu_lib, case, dtype):
+    seqlens, hq, hkv, causal, window, dist = case
+    inp = random_case(seqlens, hq, hkv, 64, dtype, seed=sum(seqlens) + hq, causal=causal, window=window,
+                      sink_dist=dist, scale=0.125)
+    _full_case(gpu_lib, inp, f"small {case} {dtype}")
+
+
+def test_unequal_lengths_bottom_right(gpu_lib):
+    """N_q != N_k per sequence: causal and window align the last query with the last key."""
+    torch.manual_seed(5)
+    lq, lk = [100, 7, 130, 0], [160, 3, 130, 50]
+    hq, hkv = 4, 2
+    for dtype, tol in ((torch.float32, 1e-5), (torch.bfloat16, 2e-2)):
+        for window in (0, 40):
+            q = torch.randn(sum(lq), hq, 64).to(dtype)
+            k = torch.randn(sum(lk), hkv, 64).to(dtype)
+            v = torch.randn(sum(lk), hkv, 64).to(dtype)
+            do = torch.randn(sum(lq), hq, 64).to(dtype)
+            s = torch.randn(hq)
+            cq = torch.tensor(np.cumsum([0] + lq), dtype=torch.int32)
+            ck = torch.tensor(np.cumsum([0] + lk), dtype=torch.int32)
+            o, lse = gpu_lib.fwd(q.cuda(), k.cuda(), v.cuda(), s.cuda(), cq.cuda(), ck.cuda(), max(lq), max(lk),
+                                 0.125, True, window)
+            dq, dk, dv, ds = gpu_lib.bwd(q.cuda(), k.cuda(), v.cuda(), s.cuda(), o, lse, do.cuda(), cq.cuda(),
+                                         ck.cuda(), max(lq), max(lk), 0.125, True, window)
+            ref = oracle.sink_attention_backward(q, k, v, s, do, cq, ck, 0.125, True, window)
+            gpu = {n: t.float().cpu().numpy().astype(np.float64)
+                   for n, t in dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv, dsinks=ds).items()}
+            compare(gpu, ref, ALL, tol, f"unequal lengths {dtype} w{window}")
+
+
+# ----------------------------------------------------------------------------- special cases
+def test_minus_inf_sink_is_standard_attention(gpu_lib):
+    inp = random_case([200, 131], 4, 2, 64, "fp32", seed=11)
+    inp["sinks"] = torch.full((4,), float("-inf"))
+    gpu = gpu_fwd_bwd(gpu_lib, inp)
+    ref = oracle_bwd(inp)
+    compare(gpu, ref, ("o", "lse", "dq", "dk", "dv"), 1e-5, "S_h=-inf")
+    assert np.all(gpu["dsinks"] == 0.0)
+    # and against torch's own attention for one head (float32, CPU)
+    q, k, v = inp["q"][:200, 0], inp["k"][:200, 0], inp["v"][:200, 0]
+    std = torch.nn.functional.scaled_dot_product_attention(q[None], k[None], v[None], is_causal=True,
+                                                           scale=0.125)[0]
+    assert np.max(np.abs(gpu["o"][:200, 0] - std.numpy())) < 1e-5
+
+
+def test_large_sink_absorbs_everything(gpu_lib):
+    inp = random_case([300], 2, 1, 64, "fp32", seed=12)
+    inp["sinks"] = torch.tensor([30.0, 60.0])
+    gpu = gpu_fwd_bwd(gpu_lib, inp)
+    assert np.max(np.abs(gpu["o"])) < 1e-8
+    np.testing.assert_allclose(gpu["lse"], np.array([[30.0], [60.0]]) * np.ones((1, 300)), rtol=1e-6)
+    ref = oracle_bwd(inp)
+    compare(gpu, ref, ("lse", "dsinks"), 1e-5, "S_h=30,60")
+
+
+def test_constant_v(gpu_lib):
+    inp = random_case([260], 4, 2, 64, "fp32", seed=13)
+    c = torch.randn(64)
+    inp["v"] = c.expand(260, 2, 64).contiguous()
+    gpu = gpu_fwd_bwd(gpu_lib, inp, with_bwd=False)
+    p_sink = np.exp(inp["sinks"].numpy()[:, None] - gpu["lse"])
+    np.testing.assert_allclose(gpu["o"], ((1 - p_sink).T)[:, :, None] * c.numpy(), atol=1e-5)
+
+
+def test_window_at_least_n_equals_causal(gpu_lib):
+    inp = random_case([400], 8, 2, 64, "bf16", seed=14)
+    a = gpu_fwd_bwd(gpu_lib, inp)
+    inp["window"] = 400
+    b = gpu_fwd_bwd(gpu_lib, inp)
+    for key in ("o", "lse", "dsinks"):
+        assert np.array_equal(a[key], b[key]), key
+    for key in ("dq", "dk", "dv"):
+        assert np.max(np.abs(a[key] - b[key])) <= 1e-2 * np.max(np.abs(a[key])), key
+
+
+def test_varlen_equals_separate_calls(gpu_lib):
+    lens = [130, 0, 257, 64]
+    inp = random_case(lens, 8, 2, 64, "bf16", seed=15, window=50)
+    packed = gpu_fwd_bwd(gpu_lib, inp)
+    cu = np.cumsum([0] + lens)
+    ds = np.zeros(8)
+    for b, n in enumerate(lens):
+        if n == 0:
+            continue
+        a, e = cu[b], cu[b + 1]
+        one = dict(inp, q=inp["q"][a:e], k=inp["k"][a:e], v=inp["v"][a:e], dout=inp["dout"][a:e],
+                   cu_seqlens=torch.tensor([0, n], dtype=torch.int32), max_seqlen=n)
+        g = gpu_fwd_bwd(gpu_lib, one)
+        assert np.array_equal(g["o"], packed["o"][a:e])
+        assert np.array_equal(g["lse"], packed["lse"][:, a:e])
+        for key in ("dq", "dk", "dv"):
+            assert np.max(np.abs(g[key] - packed[key][a:e])) <= 1e-2 * max(1e-30, np.max(np.abs(packed[key][a:e])))
+        ds += g["dsinks"]
+    np.testing.assert_allclose(ds, packed["dsinks"], rtol=1e-4, atol=1e-5)
+
+
+def test_gqa_equals_duplicated_kv(gpu_lib):
+    inp = random_case([300], 8, 2, 64, "fp32", seed=16)
+    a = gpu_fwd_bwd(gpu_lib, inp)
+    dup = dict(inp, k=inp["k"].repeat_interleave(4, dim=1).contiguous(),
+               v=inp["v"].repeat_interleave(4, dim=1).contiguous())
+    b = gpu_fwd_bwd(gpu_lib, dup)
+    for key in ("o", "lse", "dq", "dsinks"):
+        np.testing.assert_allclose(a[key], b[key], rtol=1e-5, atol=1e-5)
+    for key in ("dk", "dv"):
+        np.testing.assert_allclose(a[key], b[key].reshape(300, 2, 4, 64).sum(2), rtol=1e-4, atol=1e-5)
+
+
+def test_repeatability(gpu_lib):
+    """Forward and the sink gradient are bitwise repeatable; dq/dk/dv use float atomics."""
+    inp = random_case([700, 333], 8, 2, 64, "bf16", seed=17)
+    runs = [gpu_fwd_bwd(gpu_lib, inp) for _ in range(3)]
+    for r in runs[1:]:
+        for key in ("o", "lse", "dsinks"):
+            assert np.array_equal(r[key], runs[0][key]), key
+        for key in ("dq", "dk", "dv"):
+            assert np.max(np.abs(r[key] - runs[0][key])) <= 1e-2 * np.max(np.abs(runs[0][key])), key
+
+
+def test_autograd_wrapper(gpu_lib):
+    inp = to_dev(random_case([150, 90], 4, 2, 64, "fp32", seed=18))
+    q, k, v, s = (inp[n].clone().requires_grad_(True) for n in ("q", "k", "v", "sinks"))
+    o = gpu_lib.sink_attention(q, k, v, s, inp["cu_seqlens"], softmax_scale=0.125)
+    (o * inp["dout"]).sum().backward()
+    ref = oracle.sink_attention_backward(inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(), inp["sinks"].cpu(),
+                                         inp["dout"].cpu(), [0, 150, 240], [0, 150, 240], 0.125, True, 0)
+    for name, t in (("dq", q.grad), ("dk", k.grad), ("dv", v.grad), ("dsinks", s.grad)):
+        from _parity import relerr
+        assert relerr(t.double().cpu().numpy(), ref[name]) < 1e-5, name
+
+
+def test_empty_batch_rows(gpu_lib):
+    """All sequences empty: nothing to compute, the sink gradient is 0."""
+    q = torch.zeros(0, 4, 64, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(0, 2, 64, dtype=torch.bfloat16, device="cuda")
+    s = torch.randn(4, device="cuda")
+    cu = torch.zeros(3, dtype=torch.int32, device="cuda")
+    o, lse = gpu_lib.fwd(q, k, k, s, cu, cu, 0, 0, 0.125, True, 0)
+    dq, dk, dv, ds = gpu_lib.bwd(q, k, k, s, o, lse, q, cu, cu, 0, 0, 0.125, True, 0)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and torch.all(ds == 0)
+
+
+# ----------------------------------------------------------------------------- full-size workloads
+def _sample_rows(cu, n, rng, extra=()):
+    rows = set(int(x) for x in rng.choice(cu[-1], size=min(n, cu[-1]), replace=False))
+    for b in range(len(cu) - 1):
+        a, e = cu[b], cu[b + 1]
+        for r in (a, a + 1, a + 127, a + 128, e - 2, e - 1, *[a + x for x in extra]):
+            if a <= r < e:
+                rows.add(int(r))
+    return np.array(sorted(rows))
+
+
+def test_gptoss_4k_group0(gpu_lib):
+    """4k causal GPT-OSS shape: every output of kv group 0 (8 query heads)."""
+    inp = make_inputs(WORKLOADS["gptoss_4k"])
+    print("[case] gptoss_4k", flush=True)
+    gpu = gpu_fwd_bwd(gpu_lib, inp)
+    ref = oracle_bwd(inp, heads=range(8))
+    for key in ("dk", "dv"):
+        ref[key][:, 1:] = np.nan
+    compare(gpu, ref, ALL, TOL["bf16"], "gptoss_4k group 0")
+
+
+def test_window_16k_groups(gpu_lib):
+    inp = make_inputs(WORKLOADS["window_16k"])
+    print("[case] window_16k", flush=True)
+    gpu = gpu_fwd_bwd(gpu_lib, inp)
+    ref = oracle_bwd(inp, heads=list(range(8)) + list(range(56, 64)))
+    for key in ("dk", "dv"):
+        ref[key][:, 1:7] = np.nan
+    compare(gpu, ref, ALL, TOL["bf16"], "window_16k groups 0,7")
+
+
+def _one_head_sampled(als, inp, label, head=0, n_rows=384, seed=0):
+    """One query head: O, LSE, dQ on sampled rows; dS_h; dK, dV of that head alone on
+    sampled keys (the GPU backward is rerun with dO zero for the other heads, which
+    removes their dK/dV contributions exactly)."""
+    rng = np.random.default_rng(seed)
+    cu = [int(x) for x in inp["cu_seqlens"]]
+    rows = _sample_rows(cu, n_rows, rng)
+    keys = _sample_rows(cu, n_rows, rng)
+    print(f"[case] {label}", flush=True)
+    gpu = gpu_fwd_bwd(als, inp)
+    ref = oracle_bwd(inp, heads=[head], q_rows=rows)
+    compare(gpu, ref, ("o", "lse", "dq"), TOL["bf16"], f"{label} head {head} sampled rows")
+    do = torch.zeros_like(inp["dout"])
+    do[:, head] = inp["dout"][:, head]
+    gpu1 = gpu_fwd_bwd(als, inp, dout=do)
+    ref1 = oracle_bwd(inp, heads=[head], k_rows=keys)
+    g = head // (inp["q"].shape[1] // inp["k"].shape[1])
+    for key in ("dk", "dv"):
+        mask = np.ones(ref1[key].shape[1], bool)
+        mask[g] = False
+        ref1[key][:, mask] = np.nan
+    ref1["dsinks"] = ref1["dsinks"]
+    compare(gpu1, ref1, ("dk", "dv", "dsinks"), TOL["bf16"], f"{label} head {head} sampled keys")
+    np.testing.assert_array_equal(gpu1["dsinks"][head], gpu["dsinks"][head])
+
+
+def test_long_20k_sampled(gpu_lib):
+    _one_head_sampled(gpu_lib, make_inputs(WORKLOADS["long_20k"]), "long_20k", head=5)
+
+
+def test_varlen_full_layer_sampled(gpu_lib):
+    _one_head_sampled(gpu_lib, make_inputs(WORKLOADS["varlen"], layer=0), "varlen full", head=9)
+
+
+def test_varlen_window_layer_group(gpu_lib):
+    inp = make_inputs(WORKLOADS["varlen"], layer=1)
+    print("[case] varlen window", flush=True)
+    gpu = gpu_fwd_bwd(gpu_lib, inp)
+    ref = oracle_bwd(inp, heads=range(8, 16))
+    for key in ("dk", "dv"):
+        ref[key][:, [0, 2, 3, 4, 5, 6, 7]] = np.nan
+    compare(gpu, ref, ALL, TOL["bf16"], "varlen window group 1")
