@@ -1,0 +1,238 @@
+"""Benchmark: sink-attention forward + backward on the GPT-OSS-20B attention shape.
+
+One step = attn_sink_fwd + attn_sink_bwd over one batch (B=1, Hq=64, Hkv=8,
+d=64, N=4096, causal, bf16, synthetic inputs resident in HBM).  Prints one JSON
+line: whole-job TFLOP/s (algorithmic: 4d FLOP forward + 10d FLOP backward per
+visible (query, key) pair per query head), the roofline of the dominant
+kernel (per-launch durations from HIP events recorded by the library on the
+launch stream over the timed region), and the CPU oracle timed on a bounded
+sample of the same workload.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (vector and MFMA)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+KERNEL_SOURCES = ["attention_learnable_sinks_amd/csrc/common.h", "attention_learnable_sinks_amd/csrc/fwd.hip",
+                  "attention_learnable_sinks_amd/csrc/bwd.hip"]
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_digest") != source_digest():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def count_pairs(seqlens, causal: bool, window: int) -> int:
+    """Visible (query, key) pairs per query head: the work unit of the FLOP count."""
+    total = 0
+    for n in seqlens:
+        for i in range(n):
+            hi = i + 1 if causal else n
+            lo = max(0, i - window + 1) if window > 0 else 0
+            total += max(0, hi - lo)
+    return total
+
+
+def cpu_baseline(inp: dict, workload, pairs: int, budget_s: float = 12.0, gpu_out=None):
+    """Time the float64 oracle on whole kv groups of the same inputs until about
+    `budget_s` seconds have been spent; report the algorithmic rate of that sample.
+    If GPU outputs are given, also report their normwise error on the sample."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+
+    group = workload.num_heads_q // workload.num_heads_kv
+    done, t_total, errs = 0, 0.0, {}
+    for g in range(workload.num_heads_kv):
+        heads = list(range(g * group, (g + 1) * group))
+        t0 = time.perf_counter()
+        ref = oracle.sink_attention_backward(inp["q"], inp["k"], inp["v"], inp["sinks"], inp["dout"],
+                                             inp["cu_seqlens"], inp["cu_seqlens"], inp["softmax_scale"],
+                                             inp["causal"], inp["window"], heads=heads)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if gpu_out is not None:
+            for name in ("o", "lse", "dq", "dk", "dv", "dsinks"):
+                r = ref[name]
+                if name in ("dk", "dv"):
+                    r = r[:, g:g + 1]
+                    x = gpu_out[name][:, g:g + 1]
+                else:
+                    x = gpu_out[name]
+                m = ~np.isnan(r)
+                e = float(np.max(np.abs(x[m] - r[m])) / np.max(np.abs(r[m])))
+                errs[name] = max(errs.get(name, 0.0), e)
+        if t_total >= budget_s:
+            break
+    flop = pairs * group * done * 4 * 64 + pairs * group * done * 10 * 64
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return dict(value=round(flop / t_total / 1e12, 6), unit="TFLOP/s", cores=int(threads), kind="oracle",
+                sample=f"{workload.name}: kv groups 0..{done - 1} ({done * group} of {workload.num_heads_q} query "
+                       f"heads), forward+backward, float64 numpy, {t_total:.1f} s"), errs
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gptoss_4k")
+    ap.add_argument("--layer", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this size first (for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library is a single-GPU kernel library "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import attention_learnable_sinks_amd as als
+    from workloads import WORKLOADS, make_inputs
+
+    als.load()
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[args.workload]
+    inp = make_inputs(w, layer=args.layer)
+    d = {k: inp[k].to(dev).contiguous() for k in ("q", "k", "v", "dout", "sinks", "cu_seqlens")}
+    cu = d["cu_seqlens"]
+    mx, scale, causal, window = inp["max_seqlen"], inp["softmax_scale"], inp["causal"], inp["window"]
+    shape = als.make_shape(d["q"], d["k"], cu, cu, mx, mx, scale, causal, window)
+    ws = torch.empty(als.bwd_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(d["q"])
+    lse = torch.empty(w.num_heads_q, w.total, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
+    dsk = torch.empty_like(d["sinks"])
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def step():
+        als.fwd(d["q"], d["k"], d["v"], d["sinks"], cu, cu, mx, mx, scale, causal, window, out=o, lse=lse)
+        als.bwd(d["q"], d["k"], d["v"], d["sinks"], o, lse, d["dout"], cu, cu, mx, mx, scale, causal, window,
+                workspace=ws, dq=dq, dk=dk, dv=dv, dsinks=dsk)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    als.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern = als.timing_read()
+    als.timing_enable(False)
+
+    pairs = count_pairs(w.seqlens, causal, window)
+    fwd_flop = 4 * 64 * pairs * w.num_heads_q
+    bwd_flop = 10 * 64 * pairs * w.num_heads_q
+    ms = (t1 - t0) * 1e3 / args.steps
+    value = (fwd_flop + bwd_flop) / (ms * 1e-3) / 1e12
+
+    per = {k: v[1] / v[0] for k, v in kern.items()}  # average ms per launch
+    fwd_ms = per.get("attn_sink_fwd_kernel", float("nan"))
+    bwd_ms = sum(v for k, v in per.items() if k != "attn_sink_fwd_kernel")
+    # Dominant kernel by time; its algorithmic work per launch.
+    dom = max(per, key=per.get)
+    elem = 2 if w.dtype == "bf16" else 4
+    t_tok = w.total
+    if dom == "attn_sink_fwd_kernel":
+        work, unit, bound, peak = fwd_flop / 1e12, "TFLOP/s", "mfma", PEAK_BF16_TFLOPS
+    elif dom == "attn_sink_bwd_dkdv_kernel":
+        work, unit, bound, peak = bwd_flop / 1e12, "TFLOP/s", "mfma", PEAK_BF16_TFLOPS
+    else:
+        hq, hkv = w.num_heads_q, w.num_heads_kv
+        byts = t_tok * hq * 64 * elem * 2 + t_tok * hq * 4 * 2  # pre: read O, dO, LSE; write D
+        work, unit, bound, peak = byts / 1e9, "GB/s", "hbm", PEAK_HBM_GBS
+    if w.dtype != "bf16" and unit == "TFLOP/s":
+        peak = PEAK_FP32_TFLOPS
+    achieved = work / (per[dom] * 1e-3)
+    roofline = dict(bound=bound, achieved=round(achieved, 3), peak=peak, unit=unit, frac=round(achieved / peak, 4),
+                    traffic=read_traffic(args.workload, dom), kernel=dom, launch_ms=round(per[dom], 5))
+
+    cpu, errs = None, {}
+    if not args.no_cpu:
+        host = {k: t.float().cpu().numpy().astype(np.float64) for k, t in
+                dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv, dsinks=dsk).items()}
+        cpu, errs = cpu_baseline(inp, w, pairs, args.cpu_budget, host)
+
+    out = {
+        "metric": "attention fwd+bwd TFLOP/s and % bf16 MFMA peak, GPT-OSS-20B shape",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": len(w.seqlens), "seqlens": list(w.seqlens)[:8],
+                   "num_heads_q": w.num_heads_q, "num_heads_kv": w.num_heads_kv, "head_dim": w.head_dim,
+                   "causal": bool(causal), "window": int(window), "softmax_scale": scale},
+        "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd": {"ms": round(fwd_ms, 5), "tflops": round(fwd_flop / (fwd_ms * 1e-3) / 1e12, 3),
+                "frac_of_peak": round(fwd_flop / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "bwd": {"ms": round(bwd_ms, 5), "tflops": round(bwd_flop / (bwd_ms * 1e-3) / 1e12, 3),
+                "frac_of_peak": round(bwd_flop / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "kernels_ms_per_launch": {k: round(v, 5) for k, v in per.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parity_on_cpu_sample": {k: float(f"{v:.3e}") for k, v in errs.items()} or None,
+        "kernel_source_digest": source_digest(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
