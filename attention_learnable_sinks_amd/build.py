@@ -21,6 +21,7 @@ ARCH = "gfx950"
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-munsafe-fp-atomics",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",  # MFMA accumulators in VGPRs: no accvgpr moves around the softmax
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
 ]

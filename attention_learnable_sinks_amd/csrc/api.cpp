@@ -17,6 +17,7 @@ const char* kernel_name(int id) {
   switch (id) {
     case K_FWD: return "attn_sink_fwd_kernel";
     case K_BWD_PRE: return "attn_sink_bwd_pre_kernel";
+    case K_BWD_DQ: return "attn_sink_bwd_dq_kernel";
     case K_BWD_DKDV: return "attn_sink_bwd_dkdv_kernel";
     case K_BWD_FINISH: return "attn_sink_bwd_finish_kernel";
     default: return "?";
@@ -153,17 +154,21 @@ attn_sink_status attn_sink_bwd(const attn_sink_shape* shape, const void* q, cons
   a.dv = dv;
   a.dsinks = dsinks;
   char* base = static_cast<char*>(workspace);
-  a.dq_acc = reinterpret_cast<float*>(base + ws.dq_acc);
-  a.dk_acc = reinterpret_cast<float*>(base + ws.dk_acc);
-  a.dv_acc = reinterpret_cast<float*>(base + ws.dv_acc);
   a.delta = reinterpret_cast<float*>(base + ws.delta);
   a.dsink_part = reinterpret_cast<float*>(base + ws.dsink_part);
+  a.dk_part = reinterpret_cast<float*>(base + ws.dk_part);
+  a.dv_part = reinterpret_cast<float*>(base + ws.dv_part);
   a.pre_blocks = ws.pre_blocks;
+  a.splits = ws.splits;
   const int fp32 = shape->dtype == ATTN_SINK_FP32;
 
   st = timed_launch(K_BWD_PRE, stream, [&] { return launch_bwd_pre(a, fp32, stream); });
   if (st != ATTN_SINK_OK) return st;
-  if (any_q && any_k) {
+  if (any_q) {
+    st = timed_launch(K_BWD_DQ, stream, [&] { return launch_bwd_dq(a, fp32, stream); });
+    if (st != ATTN_SINK_OK) return st;
+  }
+  if (any_k) {
     st = timed_launch(K_BWD_DKDV, stream, [&] { return launch_bwd_dkdv(a, fp32, stream); });
     if (st != ATTN_SINK_OK) return st;
   }

@@ -11,35 +11,31 @@
 // P is recomputed from the forward's lse (which includes the sink), so the sink
 // needs no other state in the backward.
 //
-// Three kernels on one stream:
-//   1. bwd_pre:    D_i, per-block partial sums of -P_sink_i D_i (reduced later in a
-//                  fixed order, so dS_h is bitwise reproducible), and zeroing of the
-//                  fp32 accumulators.
-//   2. bwd_dkdv:   one workgroup per (128 keys, query head).  Wavefront w owns keys
-//                  32w..32w+31 and keeps K, V in registers and dK^T, dV^T in fp32
-//                  accumulators across the query band.  Per 64-query tile, Q and dO
-//                  are staged in LDS row-major and transposed; S = Q K^T and
-//                  dP = dO V^T put the key on the lane, so P and dS feed dV^T += dO^T P
-//                  and dK^T += Q^T dS straight from registers.  dS goes through LDS
-//                  once more for dQ = dS K, which is added to an fp32 buffer with
-//                  hardware float atomics.  dK/dV of the Hq/Hkv query heads that share
-//                  a kv head are summed with float atomics at the end.
-//   3. bwd_finish: scale and round dq/dk/dv to the element type; sum dS_h partials.
+// Four kernels on one stream, none using atomics, so every output is bitwise
+// reproducible:
+//   1. bwd_pre:    D_i and per-block partial sums of -P_sink_i D_i.
+//   2. bwd_dq:     query-stationary (like the forward): per 64-key tile,
+//                  S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T, with Q and dO in
+//                  registers and K^T read from the row-major K tile by transposing
+//                  LDS loads.  dQ is written once, scaled, in the element type.
+//   3. bwd_dkdv:   key-stationary: a workgroup owns 128 keys of one kv head (32 per
+//                  wavefront, K and V in registers) and loops over the query heads of
+//                  its share of the GQA group and over the query tiles of the band:
+//                  S = Q K^T, dP = dO V^T put the key on the lane, so P and dS feed
+//                  dV^T += dO^T P and dK^T += Q^T dS from registers, with dO^T and Q^T
+//                  read transposed from row-major LDS tiles.  Under a causal mask key
+//                  tiles kt and n-1-kt are folded into one workgroup so all workgroups
+//                  carry the same work.  When the group is split over several
+//                  workgroups (to fill the GPU), each split writes an fp32 partial.
+//   4. bwd_finish: fixed-order sums of the dS_h partials and of the dK/dV partials.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace attn_sink {
 
 constexpr int kPreRows = 64;  // rows per bwd_pre workgroup
-
-__device__ inline bool visible(int i, int j, int off, int nk, int causal, int window) {
-  return j < nk && (!causal || j <= i + off) && (window <= 0 || j > i + off - window);
-}
-
-__device__ inline int xcd_remap(int x, int n) {
-  if (n % 8 != 0) return x;
-  return (x % 8) * (n / 8) + x / 8;
-}
 
 // ----------------------------------------------------------------------------- 1. preprocess
 template <typename T>
@@ -50,7 +46,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   const int row = blockIdx.x * kPreRows + tid / 4;
   const int part = tid % 4;  // 16 of the 64 columns
   float contrib = 0.f;
-  if (head < f.hq && row < f.total_q) {
+  if (row < f.total_q) {
     const size_t base = ((size_t)row * f.hq + head) * kD + part * 16;
     const T* o = static_cast<const T*>(f.o) + base;
     const T* d = static_cast<const T*>(a.dout) + base;
@@ -59,9 +55,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
     for (int e = 0; e < 16; ++e) acc += to_f32(o[e]) * to_f32(d[e]);
     acc += __shfl_xor(acc, 1);
     acc += __shfl_xor(acc, 2);
-    f32x4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) *reinterpret_cast<f32x4*>(a.dq_acc + base + 4 * e) = z;
     if (part == 0) {
       a.delta[(size_t)head * f.total_q + row] = acc;
       const float lse = f.lse[(size_t)head * f.total_q + row];
@@ -70,336 +63,375 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
       contrib = -ps * acc;
     }
   }
-  if (head < f.hkv && row < f.total_k) {
-    const size_t base = ((size_t)row * f.hkv + head) * kD + part * 16;
-    f32x4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      *reinterpret_cast<f32x4*>(a.dk_acc + base + 4 * e) = z;
-      *reinterpret_cast<f32x4*>(a.dv_acc + base + 4 * e) = z;
-    }
-  }
   // Fixed-order block reduction of the sink-gradient contributions.
   __shared__ float red[4];
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) contrib += __shfl_xor(contrib, m);
   if ((tid & 63) == 0) red[tid >> 6] = contrib;
   __syncthreads();
-  if (tid == 0 && head < f.hq) a.dsink_part[(size_t)head * a.pre_blocks + blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+  if (tid == 0) a.dsink_part[(size_t)head * a.pre_blocks + blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-// ----------------------------------------------------------------------------- 2. dK, dV (+ dQ atomics)
+// ----------------------------------------------------------------------------- 2. dQ
 template <typename T>
-struct BwdCfg {
-  static constexpr int BMB = 64;    // queries per tile
-  static constexpr int BNB = 128;   // keys per workgroup (4 wavefronts x 32)
+struct DqCfg {
+  static constexpr int BM = 128;  // query rows per workgroup (4 wavefronts x 32)
+  static constexpr int BN = 64;   // keys per tile
   static constexpr int THREADS = 256;
-  static constexpr int VEC = 16 / sizeof(T);
-  static constexpr int CPR = kD / VEC;
-  static constexpr int QSTR = sizeof(T) == 2 ? 72 : 65;    // [64 q][64 d]
-  static constexpr int TSTR = sizeof(T) == 2 ? 68 : 65;    // [64 d][64 q]
-  static constexpr int SSTR = sizeof(T) == 2 ? 136 : 129;  // [64 q][128 k] and [64 d][128 k]
-  static constexpr int Q_ELEMS = BMB * QSTR;
-  static constexpr int T_ELEMS = kD * TSTR;
-  static constexpr int S_ELEMS = BMB * SSTR;
-  static constexpr int KT_ELEMS = kD * SSTR;
-  static constexpr int ROWS = sizeof(T) == 2 ? 2 : 1;                 // rows per staging task
-  static constexpr int TASKS = (BMB / ROWS) * CPR / THREADS;          // per tensor, per thread
-  static constexpr int KT_TASKS = (BNB / ROWS) * CPR / THREADS;
+  static constexpr int TILE = tile_elems<T>(BN);
 };
 
 template <typename T>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
-  using C = BwdCfg<T>;
+__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
+  using C = DqCfg<T>;
   using M = Mfma<T>;
   constexpr int E = M::E, KS = M::KS;
   const FwdArgs& f = a.f;
-  __shared__ __attribute__((aligned(16))) T smem[2 * C::Q_ELEMS + 2 * C::T_ELEMS + C::S_ELEMS + C::KT_ELEMS];
-  __shared__ __attribute__((aligned(16))) float lse2_s[C::BMB];
-  __shared__ __attribute__((aligned(16))) float dd_s[C::BMB];
-  T* Qs = smem;
-  T* dOs = Qs + C::Q_ELEMS;
-  T* QsT = dOs + C::Q_ELEMS;
-  T* dOsT = QsT + C::T_ELEMS;
-  T* dSs = dOsT + C::T_ELEMS;
-  T* KsT = dSs + C::S_ELEMS;
+  __shared__ __attribute__((aligned(16))) T smem[4 * C::TILE];  // [buf][K, V]
 
-  const int n_hs = f.hq * f.num_seqs;
-  const int hs = xcd_remap(blockIdx.x, n_hs);
-  const int head = hs % f.hq;
-  const int b = hs / f.hq;
-  const int ktile = blockIdx.y;  // low key tiles see the most queries under a causal mask
-  const int g = head / (f.hq / f.hkv);
+  const XcdSlot slot = xcd_slot(blockIdx.x, f.hkv, f.hq / f.hkv);
+  const int b = slot.seq, g = slot.kv;
+  const int head = g * (f.hq / f.hkv) + slot.item;
+  const int tile = gridDim.y - 1 - blockIdx.y;
+  const SeqBounds sq = seq_bounds(f.cu_q, b, f.total_q);
+  const SeqBounds sk = seq_bounds(f.cu_k, b, f.total_k);
+  const int nq = sq.len, nk = sk.len, off = nk - nq;
+  const int qs = tile * C::BM;
+  if (qs >= nq) return;
+  const int qe = min(qs + C::BM, nq);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, c = lane & 31;
+  const int khi = f.causal ? clampi(qe - 1 + off + 1, 0, nk) : nk;
+  const int klo = f.window > 0 ? clampi(qs + off - f.window + 1, 0, nk) : 0;
+  const int qw = qs + 32 * w;
+  const int qw_end = min(qw + 32, nq);
+  int whi = f.causal ? clampi(qw_end - 1 + off + 1, 0, nk) : nk;
+  int wlo = f.window > 0 ? clampi(qw + off - f.window + 1, 0, nk) : 0;
+  if (qw >= nq) whi = wlo = 0;
+
+  const size_t kv_row = (size_t)f.hkv * kD, q_row = (size_t)f.hq * kD;
+  const T* kbase_p = static_cast<const T*>(f.k) + (size_t)sk.start * kv_row + g * kD;
+  const T* vbase_p = static_cast<const T*>(f.v) + (size_t)sk.start * kv_row + g * kD;
+
+  // Q and dO fragments (B operands of S^T = K Q^T and dP^T = V dO^T); lse and D of the lane's row.
+  const int qi = qw + c;
+  const bool qok = qi < nq;
+  typename M::Frag qf[kD / KS], dof[kD / KS];
+  {
+    const size_t o = ((size_t)(sq.start + (qok ? qi : 0)) * f.hq + head) * kD;
+    const T* qsrc = static_cast<const T*>(f.q) + o;
+    const T* dsrc = static_cast<const T*>(a.dout) + o;
+#pragma unroll
+    for (int s = 0; s < kD / KS; ++s) {
+      qf[s] = global_frag<T>(qsrc + KS * s + E * h, qok);
+      dof[s] = global_frag<T>(dsrc + KS * s + E * h, qok);
+    }
+  }
+  const float lse2 = qok ? f.lse[(size_t)head * f.total_q + sq.start + qi] * kLog2e : 0.f;
+  const float dd = qok ? a.delta[(size_t)head * f.total_q + sq.start + qi] : 0.f;
+  const float sl2 = f.scale * kLog2e;
+
+  f32x16 dqt[2];  // dQ^T [64 d x 32 q]
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqt[t][r] = 0.f;
+
+  const int kt_begin = klo / C::BN;
+  const int kt_end = khi > klo ? (khi + C::BN - 1) / C::BN : kt_begin;
+  Stager<T, C::BN, C::THREADS> kst, vst;
+  if (kt_begin < kt_end) {
+    kst.load(kbase_p, kv_row, kt_begin * C::BN, nk, tid);
+    vst.load(vbase_p, kv_row, kt_begin * C::BN, nk, tid);
+    kst.store(smem, tid);
+    vst.store(smem + C::TILE, tid);
+  }
+  __syncthreads();
+
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
+    const int buf = (kt - kt_begin) & 1;
+    const bool more = kt + 1 < kt_end;
+    if (more) {
+      kst.load(kbase_p, kv_row, (kt + 1) * C::BN, nk, tid);
+      vst.load(vbase_p, kv_row, (kt + 1) * C::BN, nk, tid);
+    }
+    const int kbase = kt * C::BN;
+    if (kbase < whi && kbase + C::BN > wlo) {
+      const T* Ks = smem + buf * 2 * C::TILE;
+      const T* Vs = Ks + C::TILE;
+      auto body = [&](auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        f32x16 st[2], dpt[2];  // S^T, dP^T: [64 keys x 32 q]
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            st[mt][r] = 0.f;
+            dpt[mt][r] = 0.f;
+          }
+#pragma unroll
+          for (int s = 0; s < kD / KS; ++s) {
+            st[mt] = M::mma(lds_row_frag<T>(Ks, 32 * mt + c, KS * s + E * h), qf[s], st[mt]);
+            dpt[mt] = M::mma(lds_row_frag<T>(Vs, 32 * mt + c, KS * s + E * h), dof[s], dpt[mt]);
+          }
+        }
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float pv = fast_exp2(fmaf(st[mt][r], sl2, -lse2));
+            if constexpr (!FULL)
+              pv = (qok & visible(qi, kbase + 32 * mt + crow(r, h), off, nk, f.causal, f.window)) ? pv : 0.f;
+            st[mt][r] = pv * (dpt[mt][r] - dd);  // dS^T
+          }
+        // dQ^T[d x q] += K^T[d x keys] . dS^T[keys x q]
+#pragma unroll
+        for (int s = 0; s < C::BN / KS; ++s) {
+          const typename M::Frag sf = pack_frag<T>(st, s);
+#pragma unroll
+          for (int md = 0; md < 2; ++md) dqt[md] = M::mma(lds_col_frag<T>(Ks, 32 * md, s, lane, true), sf, dqt[md]);
+        }
+      };
+      const bool full = qw + 32 <= nq && kbase + C::BN <= nk && (!f.causal || kbase + C::BN - 1 <= qw + off) &&
+                        (f.window <= 0 || kbase > qw_end - 1 + off - f.window);
+      if (full)
+        body(std::true_type{});
+      else
+        body(std::false_type{});
+    }
+    if (more) {
+      T* nb = smem + (buf ^ 1) * 2 * C::TILE;
+      kst.store(nb, tid);
+      vst.store(nb + C::TILE, tid);
+    }
+    __syncthreads();
+  }
+
+  if (qok) {
+    T* dst = static_cast<T*>(a.dq) + (size_t)(sq.start + qi) * q_row + head * kD;
+#pragma unroll
+    for (int md = 0; md < 2; ++md)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = 32 * md + crow(4 * r4, h);
+        const f32x16& t = dqt[md];
+        if constexpr (sizeof(T) == 2) {
+          bf16x4 v4 = {(bf16)(t[4 * r4] * f.scale), (bf16)(t[4 * r4 + 1] * f.scale), (bf16)(t[4 * r4 + 2] * f.scale),
+                       (bf16)(t[4 * r4 + 3] * f.scale)};
+          *reinterpret_cast<bf16x4*>(dst + d0) = v4;
+        } else {
+          f32x4 v4 = {t[4 * r4] * f.scale, t[4 * r4 + 1] * f.scale, t[4 * r4 + 2] * f.scale, t[4 * r4 + 3] * f.scale};
+          *reinterpret_cast<f32x4*>(dst + d0) = v4;
+        }
+      }
+  }
+}
+
+// ----------------------------------------------------------------------------- 3. dK, dV
+template <typename T>
+struct DkvCfg {
+  static constexpr int BMB = 64;   // queries per tile
+  static constexpr int BNB = 128;  // keys per key tile (4 wavefronts x 32)
+  static constexpr int THREADS = 256;
+  static constexpr int TILE = tile_elems<T>(BMB);
+};
+
+template <typename T>
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a) {
+  using C = DkvCfg<T>;
+  using M = Mfma<T>;
+  constexpr int E = M::E, KS = M::KS;
+  const FwdArgs& f = a.f;
+  __shared__ __attribute__((aligned(16))) T smem[4 * C::TILE];  // [buf][Q, dO]
+  __shared__ __attribute__((aligned(16))) float lse2_s[2][C::BMB];
+  __shared__ __attribute__((aligned(16))) float dd_s[2][C::BMB];
+
+  const XcdSlot slot = xcd_slot(blockIdx.x, f.hkv, a.splits);
+  const int b = slot.seq, g = slot.kv, split = slot.item;
+  const int hps = (f.hq / f.hkv) / a.splits;  // query heads per split
+  const int head0 = g * (f.hq / f.hkv) + split * hps;
 
   const SeqBounds sq = seq_bounds(f.cu_q, b, f.total_q);
   const SeqBounds sk = seq_bounds(f.cu_k, b, f.total_k);
   const int nq = sq.len, nk = sk.len, off = nk - nq;
-  const int kbase = ktile * C::BNB;
-  if (kbase >= nk) return;
-  const int kend = min(kbase + C::BNB, nk);
+  const int nkt = (nk + C::BNB - 1) / C::BNB;
+  const int fold = blockIdx.y;
+  if (fold >= (nkt + 1) / 2) return;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, c = lane & 31;
-
-  // Query band of the workgroup and of this wavefront's 32 keys.
-  const int qlo = f.causal ? clampi(kbase - off, 0, nq) : 0;
-  const int qhi = f.window > 0 ? clampi(kend - 1 - off + f.window, 0, nq) : nq;
-  const int kw = kbase + 32 * w;
-  const int kw_end = min(kw + 32, nk);
-  const bool wave_keys = kw < nk;
-  const int wqlo = f.causal ? clampi(kw - off, 0, nq) : 0;
-  const int wqhi = f.window > 0 ? clampi(kw_end - 1 - off + f.window, 0, nq) : nq;
-
-  const T* __restrict__ qp = static_cast<const T*>(f.q);
-  const T* __restrict__ kp = static_cast<const T*>(f.k);
-  const T* __restrict__ vp = static_cast<const T*>(f.v);
-  const T* __restrict__ dop = static_cast<const T*>(a.dout);
-  const size_t kv_row = (size_t)f.hkv * kD;
-  const size_t q_row = (size_t)f.hq * kD;
-
-  // K and V fragments (B operands of S = Q K^T and dP = dO V^T): lane owns key kw + c.
-  const int kj = kw + c;
-  typename M::Frag kf[kD / KS], vf[kD / KS];
-  {
-    const bool ok = kj < nk;
-    const size_t off_kv = (size_t)(sk.start + (ok ? kj : 0)) * kv_row + g * kD;
-#pragma unroll
-    for (int s = 0; s < kD / KS; ++s) {
-      if constexpr (E == 8) {
-        uint4 k4 = ok ? ld16(kp + off_kv + KS * s + E * h) : make_uint4(0, 0, 0, 0);
-        uint4 v4 = ok ? ld16(vp + off_kv + KS * s + E * h) : make_uint4(0, 0, 0, 0);
-        kf[s] = *reinterpret_cast<bf16x8*>(&k4);
-        vf[s] = *reinterpret_cast<bf16x8*>(&v4);
-      } else {
-        kf[s] = ok ? kp[off_kv + KS * s + h] : 0.f;
-        vf[s] = ok ? vp[off_kv + KS * s + h] : 0.f;
-      }
-    }
-  }
-
-  // K^T of the workgroup's 128 keys for dQ = dS K (B operand: lane owns a column d).
-#pragma unroll
-  for (int i = 0; i < C::KT_TASKS; ++i) {
-    const int task = tid + C::THREADS * i;
-    const int col = task % C::CPR, kr = task / C::CPR;
-    if constexpr (sizeof(T) == 2) {
-      uint4 r2[2];
-#pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        const int key = kbase + 2 * kr + rr;
-        r2[rr] = key < nk ? ld16(kp + (size_t)(sk.start + key) * kv_row + g * kD + col * 8) : make_uint4(0, 0, 0, 0);
-      }
-      const bf16* x0 = reinterpret_cast<const bf16*>(&r2[0]);
-      const bf16* x1 = reinterpret_cast<const bf16*>(&r2[1]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bf16x2 pr = {x0[e], x1[e]};
-        *reinterpret_cast<bf16x2*>(KsT + (col * 8 + e) * C::SSTR + 2 * kr) = pr;
-      }
-    } else {
-      const int key = kbase + kr;
-      uint4 r = key < nk ? ld16(kp + (size_t)(sk.start + key) * kv_row + g * kD + col * 4) : make_uint4(0, 0, 0, 0);
-      const float* x = reinterpret_cast<const float*>(&r);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) KsT[(col * 4 + e) * C::SSTR + kr] = x[e];
-    }
-  }
-
-  f32x16 dkt[2], dvt[2];  // [64 d x 32 keys] each, two 32x32 tiles
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dkt[t][r] = 0.f;
-      dvt[t][r] = 0.f;
-    }
-
+  const size_t kv_row = (size_t)f.hkv * kD, q_row = (size_t)f.hq * kD;
   const float sl2 = f.scale * kLog2e;
-  const int qt_begin = qlo / C::BMB;
-  const int qt_end = qhi > qlo ? (qhi + C::BMB - 1) / C::BMB : qt_begin;
+  const T* qhead_p = static_cast<const T*>(f.q) + (size_t)sq.start * q_row;
+  const T* dohead_p = static_cast<const T*>(a.dout) + (size_t)sq.start * q_row;
 
-  // Staging registers for one Q tile and one dO tile.
-  uint4 qreg[C::TASKS][C::ROWS], dreg[C::TASKS][C::ROWS];
-  float lse_r = 0.f, dd_r = 0.f;
-  auto load_regs = [&](int qt) {
-    const int qbase = qt * C::BMB;
+  const int n_phase = (nkt - 1 - fold != fold) ? 2 : 1;
+  for (int phase = 0; phase < n_phase; ++phase) {
+    const int kt = phase == 0 ? fold : nkt - 1 - fold;
+    const int kbase = kt * C::BNB;
+    const int kend = min(kbase + C::BNB, nk);
+    const int qlo = f.causal ? clampi(kbase - off, 0, nq) : 0;
+    const int qhi = f.window > 0 ? clampi(kend - 1 - off + f.window, 0, nq) : nq;
+    const int qt_begin = qlo / C::BMB;
+    const int nqt = qhi > qlo ? (qhi + C::BMB - 1) / C::BMB - qt_begin : 0;
+    const int n_it = hps * nqt;
+
+    const int kw = kbase + 32 * w;
+    const int kw_end = min(kw + 32, nk);
+    const bool wave_keys = kw < nk;
+    const int wqlo = f.causal ? clampi(kw - off, 0, nq) : 0;
+    const int wqhi = f.window > 0 ? clampi(kw_end - 1 - off + f.window, 0, nq) : nq;
+
+    // K and V fragments (B operands of S = Q K^T and dP = dO V^T): lane owns key kj.
+    const int kj = kw + c;
+    const bool kok = kj < nk;
+    typename M::Frag kf[kD / KS], vf[kD / KS];
+    {
+      const size_t o = (size_t)(sk.start + (kok ? kj : 0)) * kv_row + g * kD;
+      const T* ksrc = static_cast<const T*>(f.k) + o;
+      const T* vsrc = static_cast<const T*>(f.v) + o;
 #pragma unroll
-    for (int i = 0; i < C::TASKS; ++i) {
-      const int task = tid + C::THREADS * i;
-      const int col = task % C::CPR, rr0 = task / C::CPR;
-#pragma unroll
-      for (int rr = 0; rr < C::ROWS; ++rr) {
-        const int qi = qbase + rr0 * C::ROWS + rr;
-        const size_t o = (size_t)(sq.start + qi) * q_row + head * kD + col * C::VEC;
-        qreg[i][rr] = qi < nq ? ld16(qp + o) : make_uint4(0, 0, 0, 0);
-        dreg[i][rr] = qi < nq ? ld16(dop + o) : make_uint4(0, 0, 0, 0);
+      for (int s = 0; s < kD / KS; ++s) {
+        kf[s] = global_frag<T>(ksrc + KS * s + E * h, kok);
+        vf[s] = global_frag<T>(vsrc + KS * s + E * h, kok);
       }
     }
-    if (tid < C::BMB) {
-      const int qi = qbase + tid;
-      lse_r = qi < nq ? f.lse[(size_t)head * f.total_q + sq.start + qi] * kLog2e : 0.f;
-      dd_r = qi < nq ? a.delta[(size_t)head * f.total_q + sq.start + qi] : 0.f;
-    }
-  };
-  auto store_one = [&](T* rowmaj, T* trans, const uint4 (&reg)[C::TASKS][C::ROWS]) {
+    f32x16 dkt[2], dvt[2];  // dK^T, dV^T: [64 d x 32 keys]
 #pragma unroll
-    for (int i = 0; i < C::TASKS; ++i) {
-      const int task = tid + C::THREADS * i;
-      const int col = task % C::CPR, rr0 = task / C::CPR;
-      if constexpr (sizeof(T) == 2) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr) st16(rowmaj + (2 * rr0 + rr) * C::QSTR + col * 8, reg[i][rr]);
-        const bf16* x0 = reinterpret_cast<const bf16*>(&reg[i][0]);
-        const bf16* x1 = reinterpret_cast<const bf16*>(&reg[i][1]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          bf16x2 pr = {x0[e], x1[e]};
-          *reinterpret_cast<bf16x2*>(trans + (col * 8 + e) * C::TSTR + 2 * rr0) = pr;
-        }
-      } else {
-        const float* x = reinterpret_cast<const float*>(&reg[i][0]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          rowmaj[rr0 * C::QSTR + col * 4 + e] = x[e];
-          trans[(col * 4 + e) * C::TSTR + rr0] = x[e];
-        }
+      for (int r = 0; r < 16; ++r) {
+        dkt[t][r] = 0.f;
+        dvt[t][r] = 0.f;
       }
-    }
-  };
 
-  if (qt_begin < qt_end) load_regs(qt_begin);
-  for (int qt = qt_begin; qt < qt_end; ++qt) {
-    store_one(Qs, QsT, qreg);
-    store_one(dOs, dOsT, dreg);
-    if (tid < C::BMB) {
-      lse2_s[tid] = lse_r;
-      dd_s[tid] = dd_r;
-    }
-    __syncthreads();  // (A) tile staged; the previous tile's dQ reads of dSs are done
-    if (qt + 1 < qt_end) load_regs(qt + 1);
-
-    const int qbase = qt * C::BMB;
-    const int qlast = min(qbase + C::BMB, nq) - 1;
-    const bool active = wave_keys && qbase < wqhi && qlast >= wqlo;
-    f32x16 pt[2], dst[2];  // P and dS, [32 q x 32 keys] x 2, key on the lane
-    if (active) {
-      f32x16 sacc[2], dpacc[2];
-#pragma unroll
-      for (int mq = 0; mq < 2; ++mq) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sacc[mq][r] = 0.f;
-          dpacc[mq][r] = 0.f;
-        }
-#pragma unroll
-        for (int s = 0; s < kD / KS; ++s) {
-          sacc[mq] = M::mma(lds_frag<T>(Qs + (32 * mq + c) * C::QSTR + KS * s + E * h), kf[s], sacc[mq]);
-          dpacc[mq] = M::mma(lds_frag<T>(dOs + (32 * mq + c) * C::QSTR + KS * s + E * h), vf[s], dpacc[mq]);
-        }
+    Stager<T, C::BMB, C::THREADS> qst, dost;
+    float lse_r = 0.f, dd_r = 0.f;
+    auto stage = [&](int it) {
+      const int hd = head0 + it / nqt;
+      const int qt = qt_begin + it % nqt;
+      qst.load(qhead_p + hd * kD, q_row, qt * C::BMB, nq, tid);
+      dost.load(dohead_p + hd * kD, q_row, qt * C::BMB, nq, tid);
+      if (tid < C::BMB) {
+        const int qi = qt * C::BMB + tid;
+        lse_r = qi < nq ? f.lse[(size_t)hd * f.total_q + sq.start + qi] * kLog2e : 0.f;
+        dd_r = qi < nq ? a.delta[(size_t)hd * f.total_q + sq.start + qi] : 0.f;
       }
-      const bool full = qbase + C::BMB <= nq && kw_end == kw + 32 &&
-                        (!f.causal || kw + 31 <= qbase + off) &&
-                        (f.window <= 0 || kw > qlast + off - f.window);
+    };
+    auto commit = [&](int buf) {
+      qst.store(smem + buf * 2 * C::TILE, tid);
+      dost.store(smem + buf * 2 * C::TILE + C::TILE, tid);
+      if (tid < C::BMB) {
+        lse2_s[buf][tid] = lse_r;
+        dd_s[buf][tid] = dd_r;
+      }
+    };
+
+    if (n_it > 0) {
+      stage(0);
+      commit(0);
+    }
+    __syncthreads();
+    for (int it = 0; it < n_it; ++it) {
+      const int buf = it & 1;
+      const bool more = it + 1 < n_it;
+      if (more) stage(it + 1);
+      const int qbase = (qt_begin + it % nqt) * C::BMB;
+      const int qlast = min(qbase + C::BMB, nq) - 1;
+      if (wave_keys && qbase < wqhi && qlast >= wqlo) {
+        const T* Qs = smem + buf * 2 * C::TILE;
+        const T* dOs = Qs + C::TILE;
+        auto body = [&](auto full_tag) {
+          constexpr bool FULL = decltype(full_tag)::value;
+          f32x16 pt[2], dst[2];  // P, dS: [64 q x 32 keys], key on the lane
 #pragma unroll
-      for (int mq = 0; mq < 2; ++mq)
+          for (int mq = 0; mq < 2; ++mq) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              pt[mq][r] = 0.f;
+              dst[mq][r] = 0.f;
+            }
+#pragma unroll
+            for (int s = 0; s < kD / KS; ++s) {
+              pt[mq] = M::mma(lds_row_frag<T>(Qs, 32 * mq + c, KS * s + E * h), kf[s], pt[mq]);
+              dst[mq] = M::mma(lds_row_frag<T>(dOs, 32 * mq + c, KS * s + E * h), vf[s], dst[mq]);
+            }
+          }
+#pragma unroll
+          for (int mq = 0; mq < 2; ++mq)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const int ql = 32 * mq + crow(4 * r4, h);  // 4 consecutive query rows
+              const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2_s[buf][ql]);
+              const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dd_s[buf][ql]);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = 4 * r4 + e;
+                float pv = fast_exp2(fmaf(pt[mq][r], sl2, -l4[e]));
+                if constexpr (!FULL) {
+                  const int qi = qbase + ql + e;
+                  pv = ((qi < nq) & visible(qi, kj, off, nk, f.causal, f.window)) ? pv : 0.f;
+                }
+                pt[mq][r] = pv;
+                dst[mq][r] = pv * (dst[mq][r] - d4[e]);
+              }
+            }
+          // dV^T[d x keys] += dO^T[d x q] P[q x keys];  dK^T += Q^T dS
+#pragma unroll
+          for (int s = 0; s < C::BMB / KS; ++s) {
+            const typename M::Frag pf = pack_frag<T>(pt, s);
+            const typename M::Frag sf = pack_frag<T>(dst, s);
+#pragma unroll
+            for (int md = 0; md < 2; ++md) {
+              dvt[md] = M::mma(lds_col_frag<T>(dOs, 32 * md, s, lane, true), pf, dvt[md]);
+              dkt[md] = M::mma(lds_col_frag<T>(Qs, 32 * md, s, lane, true), sf, dkt[md]);
+            }
+          }
+        };
+        const bool full = qbase + C::BMB <= nq && kw + 32 <= nk && (!f.causal || kw + 31 <= qbase + off) &&
+                          (f.window <= 0 || kw > qlast + off - f.window);
+        if (full)
+          body(std::true_type{});
+        else
+          body(std::false_type{});
+      }
+      if (more) commit(buf ^ 1);
+      __syncthreads();
+    }
+
+    // Lane owns key kj; register r of tile md holds d = 32 md + crow(r, h).
+    if (kok) {
+      const size_t o = (size_t)(sk.start + kj) * kv_row + g * kD;
+#pragma unroll
+      for (int md = 0; md < 2; ++md)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const int ql = 32 * mq + crow(4 * r4, h);  // 4 consecutive query rows
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2_s + ql);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dd_s + ql);
+          const int d0 = 32 * md + crow(4 * r4, h);
+          const f32x16& tk = dkt[md];
+          const f32x16& tv = dvt[md];
+          if (a.splits == 1) {
+            T* dk = static_cast<T*>(a.dk) + o + d0;
+            T* dv = static_cast<T*>(a.dv) + o + d0;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * r4 + e;
-            float pv = fast_exp2(sacc[mq][r] * sl2 - l4[e]);
-            if (!full && !(qbase + ql + e < nq && visible(qbase + ql + e, kj, off, nk, f.causal, f.window))) pv = 0.f;
-            pt[mq][r] = pv;
-            dst[mq][r] = pv * (dpacc[mq][r] - d4[e]);
+            for (int e = 0; e < 4; ++e) {
+              dk[e] = from_f32<T>(tk[4 * r4 + e] * f.scale);
+              dv[e] = from_f32<T>(tv[4 * r4 + e]);
+            }
+          } else {
+            const size_t so = (size_t)split * f.total_k * kv_row + o + d0;
+            *reinterpret_cast<f32x4*>(a.dk_part + so) = f32x4{tk[4 * r4], tk[4 * r4 + 1], tk[4 * r4 + 2], tk[4 * r4 + 3]};
+            *reinterpret_cast<f32x4*>(a.dv_part + so) = f32x4{tv[4 * r4], tv[4 * r4 + 1], tv[4 * r4 + 2], tv[4 * r4 + 3]};
           }
         }
-      // dV^T[d x keys] += dO^T[d x q] P[q x keys];  dK^T += Q^T dS
-#pragma unroll
-      for (int s = 0; s < C::BMB / KS; ++s) {
-        const typename M::Frag pf = pack_frag<T>(pt, s);
-        const typename M::Frag sf = pack_frag<T>(dst, s);
-#pragma unroll
-        for (int md = 0; md < 2; ++md) {
-          const T* rd = dOsT + (32 * md + c) * C::TSTR;
-          const T* rq = QsT + (32 * md + c) * C::TSTR;
-          const int k0 = kc(E * s, h), k1 = kc(E * s + (E == 8 ? 4 : 0), h);
-          dvt[md] = M::mma(lds_frag_split<T>(rd + k0, rd + k1), pf, dvt[md]);
-          dkt[md] = M::mma(lds_frag_split<T>(rq + k0, rq + k1), sf, dkt[md]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int mq = 0; mq < 2; ++mq)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dst[mq][r] = 0.f;
     }
-    // dS -> LDS as [q][key] for dQ = dS K.
-#pragma unroll
-    for (int mq = 0; mq < 2; ++mq)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dSs[(32 * mq + crow(r, h)) * C::SSTR + 32 * w + c] = from_f32<T>(dst[mq][r]);
-    __syncthreads();  // (B) dSs complete; all reads of Qs/dOs for this tile are done
-
-    // dQ tile [32 q x 32 d] per wavefront over the 128 keys, accumulated with atomics.
-    {
-      const int mq = w >> 1, md = w & 1;
-      f32x16 dqa;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dqa[r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < C::BNB / KS; ++s)
-        dqa = M::mma(lds_frag<T>(dSs + (32 * mq + c) * C::SSTR + KS * s + E * h),
-                     lds_frag<T>(KsT + (32 * md + c) * C::SSTR + KS * s + E * h), dqa);
-      float* dq_base = a.dq_acc + (size_t)head * kD + 32 * md + c;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = qbase + 32 * mq + crow(r, h);
-        if (qi < nq) atomicAdd(dq_base + (size_t)(sq.start + qi) * q_row, dqa[r]);
-      }
-    }
-  }
-
-  // dK^T / dV^T: lane owns key kj; register r of tile md holds d = 32 md + crow(r, h).
-  if (kj < nk && qt_begin < qt_end) {
-    float* dkb = a.dk_acc + (size_t)(sk.start + kj) * kv_row + g * kD;
-    float* dvb = a.dv_acc + (size_t)(sk.start + kj) * kv_row + g * kD;
-#pragma unroll
-    for (int md = 0; md < 2; ++md)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        atomicAdd(dkb + 32 * md + crow(r, h), dkt[md][r]);
-        atomicAdd(dvb + 32 * md + crow(r, h), dvt[md][r]);
-      }
   }
 }
 
-// ----------------------------------------------------------------------------- 3. finish
+// ----------------------------------------------------------------------------- 4. finish
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_finish_kernel(BwdArgs a) {
   const FwdArgs& f = a.f;
-  const size_t nq4 = (size_t)f.total_q * f.hq * kD / 4;
-  const size_t nk4 = (size_t)f.total_k * f.hkv * kD / 4;
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < nq4) {
-    const f32x4 x = reinterpret_cast<const f32x4*>(a.dq_acc)[i];
-    T* d = static_cast<T*>(a.dq) + 4 * i;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) d[e] = from_f32<T>(x[e] * f.scale);
-  }
-  if (i < nk4) {
-    const f32x4 x = reinterpret_cast<const f32x4*>(a.dk_acc)[i];
-    const f32x4 y = reinterpret_cast<const f32x4*>(a.dv_acc)[i];
-    T* dk = static_cast<T*>(a.dk) + 4 * i;
-    T* dv = static_cast<T*>(a.dv) + 4 * i;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      dk[e] = from_f32<T>(x[e] * f.scale);
-      dv[e] = from_f32<T>(y[e]);
-    }
-  }
   if (blockIdx.x == 0) {
     for (int hh = threadIdx.x; hh < f.hq; hh += blockDim.x) {
       const float* part = a.dsink_part + (size_t)hh * a.pre_blocks;
@@ -408,29 +440,57 @@ __global__ __launch_bounds__(256) void bwd_finish_kernel(BwdArgs a) {
       a.dsinks[hh] = s;
     }
   }
+  if (a.splits > 1) {
+    const size_t n4 = (size_t)f.total_k * f.hkv * kD / 4;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x) {
+      f32x4 sk = reinterpret_cast<const f32x4*>(a.dk_part)[i];
+      f32x4 sv = reinterpret_cast<const f32x4*>(a.dv_part)[i];
+      for (int s = 1; s < a.splits; ++s) {
+        sk += reinterpret_cast<const f32x4*>(a.dk_part)[i + s * n4];
+        sv += reinterpret_cast<const f32x4*>(a.dv_part)[i + s * n4];
+      }
+      T* dk = static_cast<T*>(a.dk) + 4 * i;
+      T* dv = static_cast<T*>(a.dv) + 4 * i;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dk[e] = from_f32<T>(sk[e] * f.scale);
+        dv[e] = from_f32<T>(sv[e]);
+      }
+    }
+  }
 }
 
 // ----------------------------------------------------------------------------- launchers
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+int bwd_head_splits(int hq, int hkv, int total_k) {
+  // About total_k / 256 folded pairs of 128-key tiles per kv head; split the GQA
+  // group over more workgroups until there are at least two per CU.
+  const int group = hq / hkv;
+  long long pairs = (total_k + 255) / 256;
+  if (pairs < 1) pairs = 1;
+  int s = 1;
+  while (s < group && group % (2 * s) == 0 && pairs * hkv * s < 512) s *= 2;
+  return s;
+}
+
 BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k) {
   BwdWorkspace w;
-  const int rows = total_q > total_k ? total_q : total_k;
+  const int rows = total_q > 0 ? total_q : 1;
   w.pre_blocks = (rows + kPreRows - 1) / kPreRows;
-  if (w.pre_blocks == 0) w.pre_blocks = 1;
+  w.splits = bwd_head_splits(hq, hkv, total_k);
   size_t o = 0;
-  w.dq_acc = o;      o = align256(o + (size_t)total_q * hq * kD * 4);
-  w.dk_acc = o;      o = align256(o + (size_t)total_k * hkv * kD * 4);
-  w.dv_acc = o;      o = align256(o + (size_t)total_k * hkv * kD * 4);
   w.delta = o;       o = align256(o + (size_t)hq * total_q * 4);
   w.dsink_part = o;  o = align256(o + (size_t)hq * w.pre_blocks * 4);
+  const size_t part = w.splits > 1 ? (size_t)w.splits * total_k * hkv * kD * 4 : 0;
+  w.dk_part = o;     o = align256(o + part);
+  w.dv_part = o;     o = align256(o + part);
   w.total = o;
   return w;
 }
 
 hipError_t launch_bwd_pre(const BwdArgs& a, int fp32, hipStream_t stream) {
-  const int heads = a.f.hq > a.f.hkv ? a.f.hq : a.f.hkv;
-  dim3 grid(a.pre_blocks, heads);
+  dim3 grid(a.pre_blocks, a.f.hq);
   if (fp32)
     hipLaunchKernelGGL(bwd_pre_kernel<float>, grid, dim3(256), 0, stream, a);
   else
@@ -438,10 +498,21 @@ hipError_t launch_bwd_pre(const BwdArgs& a, int fp32, hipStream_t stream) {
   return hipGetLastError();
 }
 
+hipError_t launch_bwd_dq(const BwdArgs& a, int fp32, hipStream_t stream) {
+  const int tiles = (a.f.max_q + DqCfg<bf16>::BM - 1) / DqCfg<bf16>::BM;
+  if (tiles == 0) return hipSuccess;
+  dim3 grid(a.f.hq * a.f.num_seqs, tiles);
+  if (fp32)
+    hipLaunchKernelGGL(bwd_dq_kernel<float>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(bwd_dq_kernel<bf16>, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int fp32, hipStream_t stream) {
-  const int ktiles = (a.f.max_k + BwdCfg<bf16>::BNB - 1) / BwdCfg<bf16>::BNB;
-  if (ktiles == 0 || a.f.num_seqs == 0) return hipSuccess;
-  dim3 grid(a.f.hq * a.f.num_seqs, ktiles);
+  const int ktiles = (a.f.max_k + DkvCfg<bf16>::BNB - 1) / DkvCfg<bf16>::BNB;
+  if (ktiles == 0) return hipSuccess;
+  dim3 grid(a.f.hkv * a.splits * a.f.num_seqs, (ktiles + 1) / 2);
   if (fp32)
     hipLaunchKernelGGL(bwd_dkdv_kernel<float>, grid, dim3(256), 0, stream, a);
   else
@@ -450,15 +521,17 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int fp32, hipStream_t stream) {
 }
 
 hipError_t launch_bwd_finish(const BwdArgs& a, int fp32, hipStream_t stream) {
-  const size_t nq4 = (size_t)a.f.total_q * a.f.hq * kD / 4;
-  const size_t nk4 = (size_t)a.f.total_k * a.f.hkv * kD / 4;
-  size_t n = nq4 > nk4 ? nq4 : nk4;
-  if (n == 0) n = 1;
-  dim3 grid((unsigned)((n + 255) / 256));
+  size_t blocks = 1;
+  if (a.splits > 1) {
+    const size_t n4 = (size_t)a.f.total_k * a.f.hkv * kD / 4;
+    blocks = (n4 + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks == 0) blocks = 1;
+  }
   if (fp32)
-    hipLaunchKernelGGL(bwd_finish_kernel<float>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_finish_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(bwd_finish_kernel<bf16>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_finish_kernel<bf16>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -11,6 +11,12 @@
 // A contraction only needs A and B to agree on which logical k each (h, slot)
 // carries, so when a C tile is fed back as an operand, its row index becomes the
 // k index through the permutation kc(f, h) below.
+//
+// LDS tiles are row-major with 64 columns.  bf16 tiles swizzle their 16-byte
+// chunks (chunk c of row r is stored at c ^ swz(r)) so that both access patterns
+// used on them are free of bank conflicts: eight consecutive rows read at the same
+// column (ds_read_b128), and four consecutive rows x 32 bytes read by a 16-lane
+// group (ds_read_b64_tr_b16).  fp32 tiles use a padded stride of 65 words.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -26,6 +32,7 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -68,22 +75,57 @@ __device__ inline T from_f32(float x) { return (T)x; }  // bf16: round to neares
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Fragment of E consecutive elements from LDS (16 B for bf16, 4 B for fp32).
+// ---------------------------------------------------------------- LDS tile layout
 template <typename T>
-__device__ inline typename Mfma<T>::Frag lds_frag(const T* p) {
-  return *reinterpret_cast<const typename Mfma<T>::Frag*>(p);
+struct Tile;
+
+template <>
+struct Tile<bf16> {
+  static constexpr int ELEMS_PER_ROW = 64;
+  __device__ static inline int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+  // element offset of (row, col); col % 4 == 0 keeps a 4-element run inside one chunk
+  __device__ static inline int off(int r, int c) { return r * 64 + ((((c >> 3) ^ swz(r)) << 3) | (c & 7)); }
+};
+
+template <>
+struct Tile<float> {
+  static constexpr int ELEMS_PER_ROW = 65;
+  __device__ static inline int off(int r, int c) { return r * 65 + c; }
+};
+
+template <typename T>
+constexpr int tile_elems(int rows) {
+  return rows * Tile<T>::ELEMS_PER_ROW;
 }
 
-// Fragment whose slots e < 4 and e >= 4 come from two runs of 4 elements
-// (bf16 only: two 8-byte reads).  For fp32 (E = 1) only p0 is used.
+// Operand whose lane holds row `row` and k-slots [col, col + E) of a tile
+// (the k index runs along the row: contiguous).
 template <typename T>
-__device__ inline typename Mfma<T>::Frag lds_frag_split(const T* p0, const T* p1) {
+__device__ inline typename Mfma<T>::Frag lds_row_frag(const T* tile, int row, int col) {
+  return *reinterpret_cast<const typename Mfma<T>::Frag*>(tile + Tile<T>::off(row, col));
+}
+
+// Operand whose lane holds COLUMN m0 + lane%32 of a tile and, in its k-slots, rows
+// of the tile: rows kc(E*s + e, h) when `perm` (a C tile fed back as operand),
+// else KS*s + E*h + e.  bf16 uses two transposing reads (ds_read_b64_tr_b16): in
+// each 16-lane group, source lane u reads row r0 + u/4 at columns c0 + 4*(u%4) ..+3,
+// and output lane t receives rows r0 .. r0+3 at column c0 + t.
+template <typename T>
+__device__ inline typename Mfma<T>::Frag lds_col_frag(const T* tile, int m0, int s, int lane, bool perm) {
+  const int h = lane >> 5;
   if constexpr (Mfma<T>::E == 8) {
-    bf16x4 a = *reinterpret_cast<const bf16x4*>(p0);
-    bf16x4 b = *reinterpret_cast<const bf16x4*>(p1);
-    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    const int g = lane >> 4, t = lane & 15;
+    const int r0 = perm ? kc(8 * s, h) : 16 * s + 8 * h;
+    const int r1 = perm ? kc(8 * s + 4, h) : 16 * s + 8 * h + 4;
+    const int c = m0 + 16 * (g & 1) + 4 * (t & 3);
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + Tile<bf16>::off(r0 + (t >> 2), c)));
+    i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + Tile<bf16>::off(r1 + (t >> 2), c)));
+    bf16x4 ab = __builtin_bit_cast(bf16x4, a), bb = __builtin_bit_cast(bf16x4, b);
+    return bf16x8{ab[0], ab[1], ab[2], ab[3], bb[0], bb[1], bb[2], bb[3]};
   } else {
-    return *p0;
+    const int row = perm ? kc(s, h) : 2 * s + h;
+    return tile[Tile<float>::off(row, m0 + (lane & 31))];
   }
 }
 
@@ -102,6 +144,42 @@ __device__ inline typename Mfma<T>::Frag pack_frag(const f32x16* c, int s) {
   }
 }
 
+// ---------------------------------------------------------------- global <-> LDS staging
+// A tile of `ROWS` rows x 64 columns moved as 16-byte chunks: CPR chunks per row.
+template <typename T, int ROWS, int THREADS>
+struct Stager {
+  static constexpr int VEC = 16 / sizeof(T);
+  static constexpr int CPR = kD / VEC;
+  static constexpr int N = ROWS * CPR / THREADS;  // chunks per thread
+  static_assert(ROWS * CPR % THREADS == 0, "tile must split evenly over the threads");
+  uint4 reg[N];
+  // rows >= nrows are zero-filled; row r of the tile is global row row0 + r, at base + row * row_stride
+  __device__ inline void load(const T* base, size_t row_stride, int row0, int nrows, int tid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int ch = tid + THREADS * i;
+      const int r = ch / CPR, col = ch % CPR;
+      reg[i] = (row0 + r < nrows) ? *reinterpret_cast<const uint4*>(base + (size_t)(row0 + r) * row_stride + col * VEC)
+                                  : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ inline void store(T* tile, int tid) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int ch = tid + THREADS * i;
+      const int r = ch / CPR, col = ch % CPR;
+      if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<uint4*>(tile + Tile<T>::off(r, col * VEC)) = reg[i];
+      } else {
+        const float* f = reinterpret_cast<const float*>(&reg[i]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tile[Tile<T>::off(r, col * VEC + e)] = f[e];
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------- misc
 __device__ inline int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 // Sequence bounds with cu_seqlens clamped into [0, total].
@@ -114,8 +192,47 @@ __device__ inline SeqBounds seq_bounds(const int* cu, int b, int total) {
   return {a, e - a};
 }
 
-// 16-byte global load / store helpers.
-__device__ inline uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
-__device__ inline void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+// Key j visible to query i (local indices; off = n_k - n_q aligns the ends).
+__device__ inline bool visible(int i, int j, int off, int nk, int causal, int window) {
+  return (j < nk) & ((causal == 0) | (j <= i + off)) & ((window <= 0) | (j > i + off - window));
+}
+
+// Workgroups are dealt to the 8 XCDs round-robin (XCD = linear index % 8).  These
+// maps turn the linear index of the workgroup's first grid dimension into
+// (sequence, kv head, item within that kv head) such that every workgroup of kv
+// head g runs on XCD g % 8: the query heads (or head splits) that read one kv
+// head's K/V share an L2, and every XCD gets the same share of each sequence.
+// `per_kv` items belong to each (sequence, kv head).  Falls back to plain order
+// when the kv heads do not divide evenly over the XCDs.
+struct XcdSlot {
+  int seq, kv, item;
+};
+__device__ inline XcdSlot xcd_slot(int x, int num_kv, int per_kv) {
+  XcdSlot r;
+  if (num_kv % 8 == 0) {
+    const int xcd = x % 8, j = x / 8;
+    const int per_xcd = (num_kv / 8) * per_kv;  // items per sequence on one XCD
+    r.seq = j / per_xcd;
+    const int rem = j % per_xcd;
+    r.kv = (rem / per_kv) * 8 + xcd;
+    r.item = rem % per_kv;
+  } else {
+    r.item = x % per_kv;
+    r.kv = (x / per_kv) % num_kv;
+    r.seq = x / (per_kv * num_kv);
+  }
+  return r;
+}
+
+// Load E consecutive elements of a global row as an MFMA operand (zeros when !ok).
+template <typename T>
+__device__ inline typename Mfma<T>::Frag global_frag(const T* p, bool ok) {
+  if constexpr (Mfma<T>::E == 8) {
+    uint4 v = ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
+    return __builtin_bit_cast(bf16x8, v);
+  } else {
+    return ok ? *p : 0.f;
+  }
+}
 
 }  // namespace attn_sink

@@ -30,28 +30,30 @@ struct BwdArgs {
   void* dv;
   float* dsinks;
   // workspace carve-up (float32, device)
-  float* dq_acc;    // [total_q, hq, 64]
-  float* dk_acc;    // [total_k, hkv, 64]
-  float* dv_acc;    // [total_k, hkv, 64]
-  float* delta;     // [hq, total_q]   D_i = <dO_i, O_i>
-  float* dsink_part;// [hq, pre_blocks]
+  float* delta;       // [hq, total_q]   D_i = <dO_i, O_i>
+  float* dsink_part;  // [hq, pre_blocks]
+  float* dk_part;     // [splits, total_k, hkv, 64] (only when splits > 1)
+  float* dv_part;     // [splits, total_k, hkv, 64] (only when splits > 1)
   int pre_blocks;
+  int splits;         // workgroups sharing one kv head's query-head group in bwd_dkdv
 };
 
 // Kernel identifiers for the opt-in timing records.
-enum KernelId { K_FWD = 0, K_BWD_PRE = 1, K_BWD_DKDV = 2, K_BWD_FINISH = 3, K_COUNT = 4 };
+enum KernelId { K_FWD = 0, K_BWD_PRE = 1, K_BWD_DQ = 2, K_BWD_DKDV = 3, K_BWD_FINISH = 4, K_COUNT = 5 };
 const char* kernel_name(int id);
 
 // Workspace layout for a backward call; offsets in bytes from the workspace base.
 struct BwdWorkspace {
-  size_t dq_acc, dk_acc, dv_acc, delta, dsink_part, total;
-  int pre_blocks;
+  size_t delta, dsink_part, dk_part, dv_part, total;
+  int pre_blocks, splits;
 };
 BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k);
+int bwd_head_splits(int hq, int hkv, int total_k);
 
 // Each launcher enqueues one kernel on `stream` and returns hipGetLastError().
 hipError_t launch_fwd(const FwdArgs& a, int fp32, hipStream_t stream);
 hipError_t launch_bwd_pre(const BwdArgs& a, int fp32, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, int fp32, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int fp32, hipStream_t stream);
 hipError_t launch_bwd_finish(const BwdArgs& a, int fp32, hipStream_t stream);
 
