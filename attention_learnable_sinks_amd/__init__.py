@@ -24,7 +24,9 @@ import torch
 __all__ = ["load", "fwd", "bwd", "bwd_workspace_bytes", "Shape", "AttnSinkError", "sink_attention",
            "timing_enable", "timing_read", "LIB_PATH"]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_sink.so")
+# ATTN_SINK_LIBRARY may point at another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("ATTN_SINK_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                               "libattn_sink.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 BF16, FP32 = 0, 1

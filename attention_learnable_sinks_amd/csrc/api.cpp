@@ -1,7 +1,7 @@
 // C ABI of the attention-with-sinks library: argument checks, workspace carve-up,
 // kernel launches and the opt-in per-kernel timing records.  The operations are
 // defined in include/attn_sink.h.
-#include "../../include/attn_sink.h"
+#include "attn_sink.h"
 
 #include <hip/hip_runtime.h>
 
@@ -79,6 +79,12 @@ attn_sink_status check_shape(const attn_sink_shape* s) {
   // grid limits: y is the tile index (<= 65535); x is heads * sequences
   if ((long long)s->num_heads_q * s->num_seqs > 0x7fffffffLL) return ATTN_SINK_ERR_UNSUPPORTED;
   if (s->max_seqlen_q > 65535LL * 128 || s->max_seqlen_k > 65535LL * 128) return ATTN_SINK_ERR_UNSUPPORTED;
+  // Each kernel reads one head of one sequence through a buffer descriptor whose
+  // byte range (rows x row pitch) must fit in 32 bits.
+  const long long esize = s->dtype == ATTN_SINK_FP32 ? 4 : 2;
+  if ((long long)s->max_seqlen_q * s->num_heads_q * kHeadDimBuilt * esize >= (1LL << 32) ||
+      (long long)s->max_seqlen_k * s->num_heads_kv * kHeadDimBuilt * esize >= (1LL << 32))
+    return ATTN_SINK_ERR_UNSUPPORTED;
   // 32-bit row indices inside the kernels
   if ((long long)s->total_q * s->num_heads_q * kHeadDimBuilt > 0x7fffffffLL * 4LL) return ATTN_SINK_ERR_UNSUPPORTED;
   return ATTN_SINK_OK;

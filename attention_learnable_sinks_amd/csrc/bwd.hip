@@ -100,7 +100,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   if (qs >= nq) return;
   const int qe = min(qs + C::BM, nq);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index (uniform)
   const int h = lane >> 5, c = lane & 31;
   const int khi = f.causal ? clampi(qe - 1 + off + 1, 0, nk) : nk;
   const int klo = f.window > 0 ? clampi(qs + off - f.window + 1, 0, nk) : 0;
@@ -141,64 +142,64 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const int kt_begin = klo / C::BN;
   const int kt_end = khi > klo ? (khi + C::BN - 1) / C::BN : kt_begin;
   Stager<T, C::BN, C::THREADS> kst, vst;
+  kst.init(kbase_p, kv_row, nk, tid);
+  vst.init(vbase_p, kv_row, nk, tid);
   if (kt_begin < kt_end) {
-    kst.load(kbase_p, kv_row, kt_begin * C::BN, nk, tid);
-    vst.load(vbase_p, kv_row, kt_begin * C::BN, nk, tid);
+    kst.load(kt_begin * C::BN);
+    vst.load(kt_begin * C::BN);
     kst.store(smem, tid);
     vst.store(smem + C::TILE, tid);
   }
   __syncthreads();
 
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
+  // One tile: S^T, dP^T, P^T, dS^T, dQ^T += K^T dS^T; FULL tiles need no mask.
+  auto body = [&](const T* Ks, const T* Vs, int kbase, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    f32x16 st[2], dpt[2];  // S^T, dP^T: [64 keys x 32 q]
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        st[mt][r] = 0.f;
+        dpt[mt][r] = 0.f;
+      }
+#pragma unroll
+      for (int s = 0; s < kD / KS; ++s) {
+        st[mt] = M::mma(lds_row_frag<T>(Ks, 32 * mt + c, KS * s + E * h), qf[s], st[mt]);
+        dpt[mt] = M::mma(lds_row_frag<T>(Vs, 32 * mt + c, KS * s + E * h), dof[s], dpt[mt]);
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pv = fast_exp2(fmaf(st[mt][r], sl2, -lse2));  // P^T
+        if constexpr (!FULL)
+          pv = (qok & visible(qi, kbase + 32 * mt + crow(r, h), off, nk, f.causal, f.window)) ? pv : 0.f;
+        st[mt][r] = pv * (dpt[mt][r] - dd);  // dS^T
+      }
+    // dQ^T[d x q] += K^T[d x keys] . dS^T[keys x q]
+#pragma unroll
+    for (int s = 0; s < C::BN / KS; ++s) {
+      const typename M::Frag sf = pack_frag<T>(st, s);
+#pragma unroll
+      for (int md = 0; md < 2; ++md) dqt[md] = M::mma(lds_col_frag<T>(Ks, 32 * md, s, lane, true), sf, dqt[md]);
+    }
+  };
+  auto step = [&](int kt, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
     const int buf = (kt - kt_begin) & 1;
     const bool more = kt + 1 < kt_end;
     if (more) {
-      kst.load(kbase_p, kv_row, (kt + 1) * C::BN, nk, tid);
-      vst.load(vbase_p, kv_row, (kt + 1) * C::BN, nk, tid);
+      kst.load((kt + 1) * C::BN);
+      vst.load((kt + 1) * C::BN);
     }
     const int kbase = kt * C::BN;
-    if (kbase < whi && kbase + C::BN > wlo) {
-      const T* Ks = smem + buf * 2 * C::TILE;
-      const T* Vs = Ks + C::TILE;
-      auto body = [&](auto full_tag) {
-        constexpr bool FULL = decltype(full_tag)::value;
-        f32x16 st[2], dpt[2];  // S^T, dP^T: [64 keys x 32 q]
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            st[mt][r] = 0.f;
-            dpt[mt][r] = 0.f;
-          }
-#pragma unroll
-          for (int s = 0; s < kD / KS; ++s) {
-            st[mt] = M::mma(lds_row_frag<T>(Ks, 32 * mt + c, KS * s + E * h), qf[s], st[mt]);
-            dpt[mt] = M::mma(lds_row_frag<T>(Vs, 32 * mt + c, KS * s + E * h), dof[s], dpt[mt]);
-          }
-        }
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float pv = fast_exp2(fmaf(st[mt][r], sl2, -lse2));
-            if constexpr (!FULL)
-              pv = (qok & visible(qi, kbase + 32 * mt + crow(r, h), off, nk, f.causal, f.window)) ? pv : 0.f;
-            st[mt][r] = pv * (dpt[mt][r] - dd);  // dS^T
-          }
-        // dQ^T[d x q] += K^T[d x keys] . dS^T[keys x q]
-#pragma unroll
-        for (int s = 0; s < C::BN / KS; ++s) {
-          const typename M::Frag sf = pack_frag<T>(st, s);
-#pragma unroll
-          for (int md = 0; md < 2; ++md) dqt[md] = M::mma(lds_col_frag<T>(Ks, 32 * md, s, lane, true), sf, dqt[md]);
-        }
-      };
-      const bool full = qw + 32 <= nq && kbase + C::BN <= nk && (!f.causal || kbase + C::BN - 1 <= qw + off) &&
-                        (f.window <= 0 || kbase > qw_end - 1 + off - f.window);
-      if (full)
-        body(std::true_type{});
-      else
-        body(std::false_type{});
+    const T* Ks = smem + buf * 2 * C::TILE;
+    if constexpr (FULL) {
+      body(Ks, Ks + C::TILE, kbase, full_tag);
+    } else {
+      if (kbase < whi && kbase + C::BN > wlo) body(Ks, Ks + C::TILE, kbase, full_tag);
     }
     if (more) {
       T* nb = smem + (buf ^ 1) * 2 * C::TILE;
@@ -206,7 +207,19 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
       vst.store(nb + C::TILE, tid);
     }
     __syncthreads();
+  };
+  // Tiles [wf_lo, wf_hi) are fully visible to all 32 rows of this wavefront.
+  int wf_lo = kt_begin, wf_hi = kt_begin;
+  if (qw + 32 <= nq) {
+    const int lo_key = f.window > 0 ? qw_end + off - f.window : 0;
+    const int hi_key = f.causal ? min(qw + off + 1, nk) : nk;
+    wf_lo = clampi(lo_key > 0 ? (lo_key + C::BN - 1) / C::BN : 0, kt_begin, kt_end);
+    wf_hi = clampi(hi_key > 0 ? hi_key / C::BN : 0, wf_lo, kt_end);
   }
+  int kt = kt_begin;
+  for (; kt < wf_lo; ++kt) step(kt, std::false_type{});
+  for (; kt < wf_hi; ++kt) step(kt, std::true_type{});
+  for (; kt < kt_end; ++kt) step(kt, std::false_type{});
 
   if (qok) {
     T* dst = static_cast<T*>(a.dq) + (size_t)(sq.start + qi) * q_row + head * kD;
@@ -259,7 +272,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
   const int fold = blockIdx.y;
   if (fold >= (nkt + 1) / 2) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index (uniform)
   const int h = lane >> 5, c = lane & 31;
   const size_t kv_row = (size_t)f.hkv * kD, q_row = (size_t)f.hq * kD;
   const float sl2 = f.scale * kLog2e;
@@ -308,11 +322,17 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
 
     Stager<T, C::BMB, C::THREADS> qst, dost;
     float lse_r = 0.f, dd_r = 0.f;
+    int staged_head = -1;
     auto stage = [&](int it) {
       const int hd = head0 + it / nqt;
       const int qt = qt_begin + it % nqt;
-      qst.load(qhead_p + hd * kD, q_row, qt * C::BMB, nq, tid);
-      dost.load(dohead_p + hd * kD, q_row, qt * C::BMB, nq, tid);
+      if (hd != staged_head) {  // uniform: new descriptors when the query head changes
+        qst.init(qhead_p + hd * kD, q_row, nq, tid);
+        dost.init(dohead_p + hd * kD, q_row, nq, tid);
+        staged_head = hd;
+      }
+      qst.load(qt * C::BMB);
+      dost.load(qt * C::BMB);
       if (tid < C::BMB) {
         const int qi = qt * C::BMB + tid;
         lse_r = qi < nq ? f.lse[(size_t)hd * f.total_q + sq.start + qi] * kLog2e : 0.f;
@@ -333,71 +353,87 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
       commit(0);
     }
     __syncthreads();
-    for (int it = 0; it < n_it; ++it) {
+    // One (head, query tile): S, dP, P, dS, dV^T += dO^T P, dK^T += Q^T dS.
+    auto body = [&](int buf, int qbase, auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
+      const T* Qs = smem + buf * 2 * C::TILE;
+      const T* dOs = Qs + C::TILE;
+      f32x16 pt[2], dst[2];  // P, dS: [64 q x 32 keys], key on the lane
+#pragma unroll
+      for (int mq = 0; mq < 2; ++mq) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          pt[mq][r] = 0.f;
+          dst[mq][r] = 0.f;
+        }
+#pragma unroll
+        for (int s = 0; s < kD / KS; ++s) {
+          pt[mq] = M::mma(lds_row_frag<T>(Qs, 32 * mq + c, KS * s + E * h), kf[s], pt[mq]);
+          dst[mq] = M::mma(lds_row_frag<T>(dOs, 32 * mq + c, KS * s + E * h), vf[s], dst[mq]);
+        }
+      }
+#pragma unroll
+      for (int mq = 0; mq < 2; ++mq)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int ql = 32 * mq + crow(4 * r4, h);  // 4 consecutive query rows
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2_s[buf][ql]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dd_s[buf][ql]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * r4 + e;
+            float pv = fast_exp2(fmaf(pt[mq][r], sl2, -l4[e]));
+            if constexpr (!FULL) {
+              const int qi = qbase + ql + e;
+              pv = ((qi < nq) & visible(qi, kj, off, nk, f.causal, f.window)) ? pv : 0.f;
+            }
+            pt[mq][r] = pv;
+            dst[mq][r] = pv * (dst[mq][r] - d4[e]);
+          }
+        }
+      // dV^T[d x keys] += dO^T[d x q] P[q x keys];  dK^T += Q^T dS
+#pragma unroll
+      for (int s = 0; s < C::BMB / KS; ++s) {
+        const typename M::Frag pf = pack_frag<T>(pt, s);
+        const typename M::Frag sf = pack_frag<T>(dst, s);
+#pragma unroll
+        for (int md = 0; md < 2; ++md) {
+          dvt[md] = M::mma(lds_col_frag<T>(dOs, 32 * md, s, lane, true), pf, dvt[md]);
+          dkt[md] = M::mma(lds_col_frag<T>(Qs, 32 * md, s, lane, true), sf, dkt[md]);
+        }
+      }
+    };
+    auto step = [&](int it, int qt, auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
       const int buf = it & 1;
       const bool more = it + 1 < n_it;
       if (more) stage(it + 1);
-      const int qbase = (qt_begin + it % nqt) * C::BMB;
-      const int qlast = min(qbase + C::BMB, nq) - 1;
-      if (wave_keys && qbase < wqhi && qlast >= wqlo) {
-        const T* Qs = smem + buf * 2 * C::TILE;
-        const T* dOs = Qs + C::TILE;
-        auto body = [&](auto full_tag) {
-          constexpr bool FULL = decltype(full_tag)::value;
-          f32x16 pt[2], dst[2];  // P, dS: [64 q x 32 keys], key on the lane
-#pragma unroll
-          for (int mq = 0; mq < 2; ++mq) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              pt[mq][r] = 0.f;
-              dst[mq][r] = 0.f;
-            }
-#pragma unroll
-            for (int s = 0; s < kD / KS; ++s) {
-              pt[mq] = M::mma(lds_row_frag<T>(Qs, 32 * mq + c, KS * s + E * h), kf[s], pt[mq]);
-              dst[mq] = M::mma(lds_row_frag<T>(dOs, 32 * mq + c, KS * s + E * h), vf[s], dst[mq]);
-            }
-          }
-#pragma unroll
-          for (int mq = 0; mq < 2; ++mq)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-              const int ql = 32 * mq + crow(4 * r4, h);  // 4 consecutive query rows
-              const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2_s[buf][ql]);
-              const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dd_s[buf][ql]);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int r = 4 * r4 + e;
-                float pv = fast_exp2(fmaf(pt[mq][r], sl2, -l4[e]));
-                if constexpr (!FULL) {
-                  const int qi = qbase + ql + e;
-                  pv = ((qi < nq) & visible(qi, kj, off, nk, f.causal, f.window)) ? pv : 0.f;
-                }
-                pt[mq][r] = pv;
-                dst[mq][r] = pv * (dst[mq][r] - d4[e]);
-              }
-            }
-          // dV^T[d x keys] += dO^T[d x q] P[q x keys];  dK^T += Q^T dS
-#pragma unroll
-          for (int s = 0; s < C::BMB / KS; ++s) {
-            const typename M::Frag pf = pack_frag<T>(pt, s);
-            const typename M::Frag sf = pack_frag<T>(dst, s);
-#pragma unroll
-            for (int md = 0; md < 2; ++md) {
-              dvt[md] = M::mma(lds_col_frag<T>(dOs, 32 * md, s, lane, true), pf, dvt[md]);
-              dkt[md] = M::mma(lds_col_frag<T>(Qs, 32 * md, s, lane, true), sf, dkt[md]);
-            }
-          }
-        };
-        const bool full = qbase + C::BMB <= nq && kw + 32 <= nk && (!f.causal || kw + 31 <= qbase + off) &&
-                          (f.window <= 0 || kw > qlast + off - f.window);
-        if (full)
-          body(std::true_type{});
-        else
-          body(std::false_type{});
+      const int qbase = qt * C::BMB;
+      if constexpr (FULL) {
+        body(buf, qbase, full_tag);
+      } else {
+        const int qlast = min(qbase + C::BMB, nq) - 1;
+        if (wave_keys && qbase < wqhi && qlast >= wqlo) body(buf, qbase, full_tag);
       }
       if (more) commit(buf ^ 1);
       __syncthreads();
+    };
+    // Query tiles [qf_lo, qf_hi) are fully visible to all 32 keys of this wavefront:
+    // past the diagonal, before the window's right edge, inside the sequence.
+    const int qt_end = qt_begin + nqt;
+    int qf_lo = qt_begin, qf_hi = qt_begin;
+    if (kw + 32 <= nk) {
+      const int lo_q = f.causal ? kw + 31 - off : 0;                      // first row seeing all 32 keys
+      const int hi_q = f.window > 0 ? min(kw - off + f.window, nq) : nq;  // rows below this see them too
+      qf_lo = clampi(lo_q > 0 ? (lo_q + C::BMB - 1) / C::BMB : 0, qt_begin, qt_end);
+      qf_hi = clampi(hi_q > 0 ? hi_q / C::BMB : 0, qf_lo, qt_end);
+    }
+    int it = 0;
+    for (int hd = 0; hd < hps; ++hd) {
+      int qt = qt_begin;
+      for (; qt < qf_lo; ++qt, ++it) step(it, qt, std::false_type{});
+      for (; qt < qf_hi; ++qt, ++it) step(it, qt, std::true_type{});
+      for (; qt < qt_end; ++qt, ++it) step(it, qt, std::false_type{});
     }
 
     // Lane owns key kj; register r of tile md holds d = 32 md + crow(r, h).

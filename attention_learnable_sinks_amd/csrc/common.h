@@ -144,24 +144,54 @@ __device__ inline typename Mfma<T>::Frag pack_frag(const f32x16* c, int s) {
   }
 }
 
+// acc + sum of the E elements of an operand fragment (bf16: four v_dot2 with (1, 1)).
+template <typename T>
+__device__ inline float frag_sum(typename Mfma<T>::Frag f, float acc) {
+  if constexpr (Mfma<T>::E == 8) {
+    const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{f[e], f[e + 1]}, ones, acc, false);
+    return acc;
+  } else {
+    return acc + f;
+  }
+}
+
 // ---------------------------------------------------------------- global <-> LDS staging
-// A tile of `ROWS` rows x 64 columns moved as 16-byte chunks: CPR chunks per row.
+// A tile of `ROWS` rows x 64 columns of one head, moved as 16-byte chunks (CPR per
+// row) with raw buffer loads: the buffer descriptor covers exactly the sequence's
+// rows of this head, so the per-thread offset is a constant VGPR, the tile offset
+// is a scalar, and chunks past the last row read as zero (buffer range checking)
+// without any branch or address arithmetic in the loop.
+constexpr int kBufferWord3 = 0x00020000;  // gfx9-family raw buffer descriptor, dword 3
+
 template <typename T, int ROWS, int THREADS>
 struct Stager {
   static constexpr int VEC = 16 / sizeof(T);
   static constexpr int CPR = kD / VEC;
   static constexpr int N = ROWS * CPR / THREADS;  // chunks per thread
   static_assert(ROWS * CPR % THREADS == 0, "tile must split evenly over the threads");
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t row_bytes;
+  uint32_t voff[N];
   uint4 reg[N];
-  // rows >= nrows are zero-filled; row r of the tile is global row row0 + r, at base + row * row_stride
-  __device__ inline void load(const T* base, size_t row_stride, int row0, int nrows, int tid) {
+  // base: element (row 0, column 0) of the head; rows are row_stride elements apart;
+  // nrows rows are readable (the caller guarantees nrows * row_stride * sizeof(T) < 2^32).
+  __device__ inline void init(const T* base, size_t row_stride, int nrows, int tid) {
+    row_bytes = (uint32_t)(row_stride * sizeof(T));
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), (short)0, (int)(nrows * row_bytes), kBufferWord3);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int ch = tid + THREADS * i;
-      const int r = ch / CPR, col = ch % CPR;
-      reg[i] = (row0 + r < nrows) ? *reinterpret_cast<const uint4*>(base + (size_t)(row0 + r) * row_stride + col * VEC)
-                                  : make_uint4(0, 0, 0, 0);
+      voff[i] = (uint32_t)(ch / CPR) * row_bytes + (uint32_t)(ch % CPR) * 16u;
     }
+  }
+  // Load the tile whose first row is row0 (rows >= nrows read as zero).
+  __device__ inline void load(int row0) {
+    const uint32_t soff = (uint32_t)row0 * row_bytes;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      reg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[i], soff, 0));
   }
   __device__ inline void store(T* tile, int tid) const {
 #pragma unroll

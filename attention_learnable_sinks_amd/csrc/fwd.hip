@@ -64,7 +64,8 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
   if (qs >= nq) return;
   const int qe = min(qs + C::BM, nq);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index (uniform)
   const int h = lane >> 5, c = lane & 31;
 
   // Key range of the workgroup and of this wavefront.
@@ -106,91 +107,88 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
   const int kt_end = khi > klo ? (khi + C::BN - 1) / C::BN : kt_begin;
 
   Stager<T, C::BN, C::THREADS> kst, vst;
+  kst.init(kbase_p, kv_row, nk, tid);
+  vst.init(vbase_p, kv_row, nk, tid);
   if (kt_begin < kt_end) {
-    kst.load(kbase_p, kv_row, kt_begin * C::BN, nk, tid);
-    vst.load(vbase_p, kv_row, kt_begin * C::BN, nk, tid);
+    kst.load(kt_begin * C::BN);
+    vst.load(kt_begin * C::BN);
     kst.store(smem, tid);
     vst.store(smem + C::TILE, tid);
   }
   __syncthreads();
 
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
+  // One tile: S^T, (mask), online softmax, O^T += V^T P^T.  FULL tiles need no mask;
+  // the masked instantiation selects per element without branches.  Both are
+  // straight-line code so the scheduler can overlap LDS reads, MFMA and exp.
+  auto body = [&](const T* Ks, const T* Vs, int kbase, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    f32x16 sacc[2];  // S^T tile [64 keys x 32 queries] as two 32x32 tiles
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < kD / KS; ++s)
+        sacc[mt] = M::mma(lds_row_frag<T>(Ks, 32 * mt + c, KS * s + E * h), qf[s], sacc[mt]);
+    }
+    if constexpr (!FULL) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sacc[mt][r] =
+              visible(qi, kbase + 32 * mt + crow(r, h), off, nk, p.causal, p.window) ? sacc[mt][r] : -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+    // Lazy rescale: the running max may trail the true max by up to kSlack (so
+    // probabilities stay <= 2^kSlack); O and l are rescaled only when some row of
+    // the wavefront exceeds that, which after the first tiles is rare.
+    if (__any(mx > m_run + kSlack)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);  // 0 when m_run = -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[mt][r] = fast_exp2(fmaf(sacc[mt][r], sl2, neg_m));
+    // O^T[d x q] += V^T[d x keys] . P^T[keys x q]; the row sum is taken from the same
+    // rounded P that multiplies V.
+#pragma unroll
+    for (int s = 0; s < C::BN / KS; ++s) {
+      const typename M::Frag pf = pack_frag<T>(sacc, s);
+      l_run = frag_sum<T>(pf, l_run);
+#pragma unroll
+      for (int md = 0; md < 2; ++md) oacc[md] = M::mma(lds_col_frag<T>(Vs, 32 * md, s, lane, true), pf, oacc[md]);
+    }
+  };
+  // One pipeline step: prefetch tile kt+1 into registers, compute tile kt from LDS,
+  // commit the prefetched tile to the other buffer, barrier.
+  auto step = [&](int kt, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
     const int buf = (kt - kt_begin) & 1;
     const bool more = kt + 1 < kt_end;
     if (more) {
-      kst.load(kbase_p, kv_row, (kt + 1) * C::BN, nk, tid);
-      vst.load(vbase_p, kv_row, (kt + 1) * C::BN, nk, tid);
+      kst.load((kt + 1) * C::BN);
+      vst.load((kt + 1) * C::BN);
     }
     const int kbase = kt * C::BN;
-    if (kbase < whi && kbase + C::BN > wlo) {
-      const T* Ks = smem + buf * 2 * C::TILE;
-      const T* Vs = Ks + C::TILE;
-      // One tile: S^T, (mask), online softmax, O^T += V^T P^T.  FULL tiles need no mask;
-      // the masked instantiation selects, without branches, per element.
-      auto body = [&](auto full_tag) {
-        constexpr bool FULL = decltype(full_tag)::value;
-        f32x16 sacc[2];  // S^T tile [64 keys x 32 queries] as two 32x32 tiles
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.f;
-#pragma unroll
-          for (int s = 0; s < kD / KS; ++s)
-            sacc[mt] = M::mma(lds_row_frag<T>(Ks, 32 * mt + c, KS * s + E * h), qf[s], sacc[mt]);
-        }
-        if constexpr (!FULL) {
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              sacc[mt][r] = visible(qi, kbase + 32 * mt + crow(r, h), off, nk, p.causal, p.window) ? sacc[mt][r]
-                                                                                                     : -INFINITY;
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-        // Lazy rescale: the running max may trail the true max by up to kSlack (so
-        // probabilities stay <= 2^kSlack); O and l are rescaled only when some row of
-        // the wavefront exceeds that, which after the first tiles is rare.
-        if (__any(mx > m_run + kSlack)) {
-          const float m_new = fmaxf(m_run, mx);
-          const float alpha = fast_exp2(m_run - m_new);  // 0 when m_run = -inf
-          l_run *= alpha;
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
-          m_run = m_new;
-        }
-        const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
-        float psum = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float pr = fast_exp2(fmaf(sacc[mt][r], sl2, neg_m));
-            sacc[mt][r] = pr;
-            psum += pr;
-          }
-        l_run += psum;
-        // O^T[d x q] += V^T[d x keys] . P^T[keys x q]
-#pragma unroll
-        for (int s = 0; s < C::BN / KS; ++s) {
-          const typename M::Frag pf = pack_frag<T>(sacc, s);
-#pragma unroll
-          for (int md = 0; md < 2; ++md)
-            oacc[md] = M::mma(lds_col_frag<T>(Vs, 32 * md, s, lane, true), pf, oacc[md]);
-        }
-      };
-      const bool full = kbase + C::BN <= nk && (!p.causal || kbase + C::BN - 1 <= qw + off) &&
-                        (p.window <= 0 || kbase > qw_end - 1 + off - p.window);
-      if (full)
-        body(std::true_type{});
-      else
-        body(std::false_type{});
+    const T* Ks = smem + buf * 2 * C::TILE;
+    if constexpr (FULL) {
+      body(Ks, Ks + C::TILE, kbase, full_tag);
+    } else {
+      if (kbase < whi && kbase + C::BN > wlo) body(Ks, Ks + C::TILE, kbase, full_tag);
     }
     if (more) {
       T* nb = smem + (buf ^ 1) * 2 * C::TILE;
@@ -198,7 +196,21 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
       vst.store(nb + C::TILE, tid);
     }
     __syncthreads();
+  };
+  // Tiles [wf_lo, wf_hi) are fully visible to every row of this wavefront: inside
+  // the window's left edge, left of the diagonal and inside the sequence.  Every
+  // wavefront runs the same number of steps (one barrier each), only the body differs.
+  int wf_lo = kt_begin, wf_hi = kt_begin;
+  if (wave_rows) {
+    const int lo_key = p.window > 0 ? qw_end + off - p.window : 0;  // first key every row sees from the left
+    const int hi_key = p.causal ? min(qw + off + 1, nk) : nk;        // keys below this are seen by every row
+    wf_lo = clampi(lo_key > 0 ? (lo_key + C::BN - 1) / C::BN : 0, kt_begin, kt_end);
+    wf_hi = clampi(hi_key > 0 ? hi_key / C::BN : 0, wf_lo, kt_end);
   }
+  int kt = kt_begin;
+  for (; kt < wf_lo; ++kt) step(kt, std::false_type{});
+  for (; kt < wf_hi; ++kt) step(kt, std::true_type{});
+  for (; kt < kt_end; ++kt) step(kt, std::false_type{});
 
   // ---- epilogue: add the sink's mass once, normalise, write O and LSE.
   const float m_use = m_run == -INFINITY ? 0.f : m_run;
