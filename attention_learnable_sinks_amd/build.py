@@ -57,6 +57,15 @@ def build(verbose: bool = False) -> str:
         objs.append(obj)
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    # A kernel template whose host-side instantiation failed leaves its launch stub
+    # undefined; catch that here rather than at load time.
+    nm = shutil.which("nm")
+    if nm:
+        und = subprocess.run([nm, "-D", "--undefined-only", tmp], capture_output=True, text=True).stdout
+        missing = [l.split()[-1] for l in und.splitlines() if "attn_sink" in l]
+        if missing:
+            os.remove(tmp)
+            raise RuntimeError(f"undefined library symbols after linking: {missing}")
     os.replace(tmp, LIB)
     return LIB
 

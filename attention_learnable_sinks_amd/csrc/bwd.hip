@@ -141,14 +141,14 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 
   const int kt_begin = klo / C::BN;
   const int kt_end = khi > klo ? (khi + C::BN - 1) / C::BN : kt_begin;
-  Stager<T, C::BN, C::THREADS> kst, vst;
-  kst.init(kbase_p, kv_row, nk, tid);
-  vst.init(vbase_p, kv_row, nk, tid);
+  TileLoader<T, C::BN, C::THREADS> kld, vld;
+  kld.init(kbase_p, kv_row, nk, tid);
+  vld.init(vbase_p, kv_row, nk, tid);
   if (kt_begin < kt_end) {
-    kst.load(kt_begin * C::BN);
-    vst.load(kt_begin * C::BN);
-    kst.store(smem, tid);
-    vst.store(smem + C::TILE, tid);
+    kld.issue(kt_begin * C::BN, smem);
+    vld.issue(kt_begin * C::BN, smem + C::TILE);
+    kld.finish();
+    vld.finish();
   }
   __syncthreads();
 
@@ -190,9 +190,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     constexpr bool FULL = decltype(full_tag)::value;
     const int buf = (kt - kt_begin) & 1;
     const bool more = kt + 1 < kt_end;
+    T* nb = smem + (buf ^ 1) * 2 * C::TILE;  // read in the previous step, before its barrier
     if (more) {
-      kst.load((kt + 1) * C::BN);
-      vst.load((kt + 1) * C::BN);
+      kld.issue((kt + 1) * C::BN, nb);
+      vld.issue((kt + 1) * C::BN, nb + C::TILE);
     }
     const int kbase = kt * C::BN;
     const T* Ks = smem + buf * 2 * C::TILE;
@@ -202,9 +203,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
       if (kbase < whi && kbase + C::BN > wlo) body(Ks, Ks + C::TILE, kbase, full_tag);
     }
     if (more) {
-      T* nb = smem + (buf ^ 1) * 2 * C::TILE;
-      kst.store(nb, tid);
-      vst.store(nb + C::TILE, tid);
+      kld.finish();
+      vld.finish();
     }
     __syncthreads();
   };
@@ -320,28 +320,29 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
         dvt[t][r] = 0.f;
       }
 
-    Stager<T, C::BMB, C::THREADS> qst, dost;
+    TileLoader<T, C::BMB, C::THREADS> qld, dold;
     float lse_r = 0.f, dd_r = 0.f;
     int staged_head = -1;
-    auto stage = [&](int it) {
+    // Start moving (head, query tile) of iteration `it` into LDS buffer `buf`.
+    auto stage = [&](int it, int buf) __device__ {
       const int hd = head0 + it / nqt;
       const int qt = qt_begin + it % nqt;
       if (hd != staged_head) {  // uniform: new descriptors when the query head changes
-        qst.init(qhead_p + hd * kD, q_row, nq, tid);
-        dost.init(dohead_p + hd * kD, q_row, nq, tid);
+        qld.init(qhead_p + hd * kD, q_row, nq, tid);
+        dold.init(dohead_p + hd * kD, q_row, nq, tid);
         staged_head = hd;
       }
-      qst.load(qt * C::BMB);
-      dost.load(qt * C::BMB);
+      qld.issue(qt * C::BMB, smem + buf * 2 * C::TILE);
+      dold.issue(qt * C::BMB, smem + buf * 2 * C::TILE + C::TILE);
       if (tid < C::BMB) {
         const int qi = qt * C::BMB + tid;
         lse_r = qi < nq ? f.lse[(size_t)hd * f.total_q + sq.start + qi] * kLog2e : 0.f;
         dd_r = qi < nq ? a.delta[(size_t)hd * f.total_q + sq.start + qi] : 0.f;
       }
     };
-    auto commit = [&](int buf) {
-      qst.store(smem + buf * 2 * C::TILE, tid);
-      dost.store(smem + buf * 2 * C::TILE + C::TILE, tid);
+    auto commit = [&](int buf) __device__ {
+      qld.finish();
+      dold.finish();
       if (tid < C::BMB) {
         lse2_s[buf][tid] = lse_r;
         dd_s[buf][tid] = dd_r;
@@ -349,12 +350,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
     };
 
     if (n_it > 0) {
-      stage(0);
+      stage(0, 0);
       commit(0);
     }
     __syncthreads();
     // One (head, query tile): S, dP, P, dS, dV^T += dO^T P, dK^T += Q^T dS.
-    auto body = [&](int buf, int qbase, auto full_tag) {
+    auto body = [&](int buf, int qbase, auto full_tag) __device__ {
       constexpr bool FULL = decltype(full_tag)::value;
       const T* Qs = smem + buf * 2 * C::TILE;
       const T* dOs = Qs + C::TILE;
@@ -403,11 +404,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
         }
       }
     };
-    auto step = [&](int it, int qt, auto full_tag) {
+    auto step = [&](int it, int qt, auto full_tag) __device__ {
       constexpr bool FULL = decltype(full_tag)::value;
       const int buf = it & 1;
       const bool more = it + 1 < n_it;
-      if (more) stage(it + 1);
+      if (more) stage(it + 1, buf ^ 1);  // that buffer was read in the previous step
       const int qbase = qt * C::BMB;
       if constexpr (FULL) {
         body(buf, qbase, full_tag);

@@ -144,6 +144,16 @@ __device__ inline typename Mfma<T>::Frag pack_frag(const f32x16* c, int s) {
   }
 }
 
+// max / sum of x over the two lane halves (lanes l and l ^ 32), via v_permlane32_swap.
+__device__ inline float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // acc + sum of the E elements of an operand fragment (bf16: four v_dot2 with (1, 1)).
 template <typename T>
 __device__ inline float frag_sum(typename Mfma<T>::Frag f, float acc) {
@@ -207,6 +217,67 @@ struct Stager {
       }
     }
   }
+};
+
+// Tile loader with one interface for both element types: issue(row0, tile) starts
+// moving rows [row0, row0 + ROWS) of the head into LDS tile `tile`, finish() makes
+// sure they have arrived (the caller then synchronises the workgroup).
+//  * bf16: direct global -> LDS buffer loads (no registers, no LDS write
+//    instructions).  One wavefront instruction fills 64 consecutive 16-byte LDS
+//    slots; each lane fetches the global chunk that the swizzled layout stores in
+//    its slot.
+//  * fp32: through registers (the padded fp32 layout is not 16-byte aligned).
+template <typename T, int ROWS, int THREADS>
+struct TileLoader;
+
+template <int ROWS, int THREADS>
+struct TileLoader<bf16, ROWS, THREADS> {
+  static constexpr int N = ROWS * 8 / THREADS;  // 16-byte slots per thread
+  static_assert(ROWS * 8 % THREADS == 0, "tile must split evenly over the threads");
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t row_bytes;
+  uint32_t voff[N];
+  int first_slot;  // first LDS slot (of 64) written by this wavefront's instructions
+  __device__ inline void init(const bf16* base, size_t row_stride, int nrows, int tid) {
+    row_bytes = (uint32_t)(row_stride * sizeof(bf16));
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), (short)0, (int)(nrows * row_bytes), kBufferWord3);
+    const int lane = tid & 63;
+    first_slot = __builtin_amdgcn_readfirstlane(tid >> 6) * N * 64;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const int slot = first_slot + n * 64 + lane;  // LDS byte offset 16 * slot in the tile
+      const int r = slot >> 3, pc = slot & 7;
+      const int col_chunk = pc ^ Tile<bf16>::swz(r);  // slot (r, pc) holds logical chunk pc ^ swz(r)
+      voff[n] = (uint32_t)r * row_bytes + (uint32_t)col_chunk * 16u;
+    }
+  }
+  __device__ inline void issue(int row0, bf16* tile) {
+    const uint32_t soff = (uint32_t)row0 * row_bytes;
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass of templated kernels must not see this builtin
+    typedef __attribute__((address_space(3))) void lds_void;
+#pragma unroll
+    for (int n = 0; n < N; ++n)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + (first_slot + n * 64) * 8), 16, voff[n], soff,
+                                               0, 0);
+#endif
+  }
+  __device__ inline void finish() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+};
+
+template <int ROWS, int THREADS>
+struct TileLoader<float, ROWS, THREADS> {
+  Stager<float, ROWS, THREADS> st;
+  float* dst;
+  int tid_;
+  __device__ inline void init(const float* base, size_t row_stride, int nrows, int tid) {
+    st.init(base, row_stride, nrows, tid);
+    tid_ = tid;
+  }
+  __device__ inline void issue(int row0, float* tile) {
+    st.load(row0);
+    dst = tile;
+  }
+  __device__ inline void finish() { st.store(dst, tid_); }
 };
 
 // ---------------------------------------------------------------- misc

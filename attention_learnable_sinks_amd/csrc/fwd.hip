@@ -11,9 +11,10 @@
 // one head; 4 wavefronts x 32 rows):
 //   * Q stays in registers as the B operand of S^T = K Q^T, so each lane owns one
 //     query row of S^T; row max / row sum are in-lane plus one lane-half swap.
-//   * K and V tiles of 64 keys are staged row-major in LDS (double-buffered with
-//     register prefetch, swizzled so the operand reads are conflict-free); the V^T
-//     operand of O^T = V^T P^T is read with transposing LDS loads.
+//   * K and V tiles of 64 keys are double-buffered row-major in LDS, loaded straight
+//     from HBM into LDS by buffer loads (swizzled so the operand reads are
+//     conflict-free); the V^T operand of O^T = V^T P^T is read with transposing LDS
+//     loads.
 //   * Online softmax in the exp2 domain (exp2(fma(s, scale*log2e, -m))).  The running
 //     max starts at the sink logit S_h*log2(e), not at -inf; the sink's own mass
 //     exp2(S_h*log2e - m) is added once at the end.  The running max is only raised
@@ -106,14 +107,14 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
   const int kt_begin = klo / C::BN;
   const int kt_end = khi > klo ? (khi + C::BN - 1) / C::BN : kt_begin;
 
-  Stager<T, C::BN, C::THREADS> kst, vst;
-  kst.init(kbase_p, kv_row, nk, tid);
-  vst.init(vbase_p, kv_row, nk, tid);
+  TileLoader<T, C::BN, C::THREADS> kld, vld;
+  kld.init(kbase_p, kv_row, nk, tid);
+  vld.init(vbase_p, kv_row, nk, tid);
   if (kt_begin < kt_end) {
-    kst.load(kt_begin * C::BN);
-    vst.load(kt_begin * C::BN);
-    kst.store(smem, tid);
-    vst.store(smem + C::TILE, tid);
+    kld.issue(kt_begin * C::BN, smem);
+    vld.issue(kt_begin * C::BN, smem + C::TILE);
+    kld.finish();
+    vld.finish();
   }
   __syncthreads();
 
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+    mx = halves_max(mx) * sl2;
     // Lazy rescale: the running max may trail the true max by up to kSlack (so
     // probabilities stay <= 2^kSlack); O and l are rescaled only when some row of
     // the wavefront exceeds that, which after the first tiles is rare.
@@ -179,9 +180,10 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
     constexpr bool FULL = decltype(full_tag)::value;
     const int buf = (kt - kt_begin) & 1;
     const bool more = kt + 1 < kt_end;
+    T* nb = smem + (buf ^ 1) * 2 * C::TILE;  // read in the previous step, before its barrier
     if (more) {
-      kst.load((kt + 1) * C::BN);
-      vst.load((kt + 1) * C::BN);
+      kld.issue((kt + 1) * C::BN, nb);
+      vld.issue((kt + 1) * C::BN, nb + C::TILE);
     }
     const int kbase = kt * C::BN;
     const T* Ks = smem + buf * 2 * C::TILE;
@@ -191,9 +193,8 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
       if (kbase < whi && kbase + C::BN > wlo) body(Ks, Ks + C::TILE, kbase, full_tag);
     }
     if (more) {
-      T* nb = smem + (buf ^ 1) * 2 * C::TILE;
-      kst.store(nb, tid);
-      vst.store(nb + C::TILE, tid);
+      kld.finish();
+      vld.finish();
     }
     __syncthreads();
   };
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
 
   // ---- epilogue: add the sink's mass once, normalise, write O and LSE.
   const float m_use = m_run == -INFINITY ? 0.f : m_run;
-  float l_tot = l_run + __shfl_xor(l_run, 32);
+  float l_tot = halves_sum(l_run);
   if (sink2 > -INFINITY) l_tot += fast_exp2(sink2 - m_use);  // m_run >= sink2: at most 1
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qi < nq) {
