@@ -180,20 +180,19 @@ def main():
     per = {k: v[1] / v[0] for k, v in kern.items()}  # average ms per launch
     fwd_ms = per.get("attn_sink_fwd_kernel", float("nan"))
     bwd_ms = sum(v for k, v in per.items() if k != "attn_sink_fwd_kernel")
-    # Dominant kernel by time; its algorithmic work per launch.
+    # Dominant kernel by time and its algorithmic work per launch: the forward does
+    # 2 GEMMs (4d FLOP per visible pair and query head), the dQ kernel 3 (S, dP, dQ:
+    # 6d) and the dK/dV kernel 4 (S, dP, dV, dK: 8d); the small kernels move bytes.
     dom = max(per, key=per.get)
     elem = 2 if w.dtype == "bf16" else 4
-    t_tok = w.total
-    if dom == "attn_sink_fwd_kernel":
-        work, unit, bound, peak = fwd_flop / 1e12, "TFLOP/s", "mfma", PEAK_BF16_TFLOPS
-    elif dom == "attn_sink_bwd_dkdv_kernel":
-        work, unit, bound, peak = bwd_flop / 1e12, "TFLOP/s", "mfma", PEAK_BF16_TFLOPS
+    t_tok, hq, hkv = w.total, w.num_heads_q, w.num_heads_kv
+    gemm_d = {"attn_sink_fwd_kernel": 4, "attn_sink_bwd_dq_kernel": 6, "attn_sink_bwd_dkdv_kernel": 8}
+    if dom in gemm_d:
+        work, unit, bound = gemm_d[dom] * 64 * pairs * hq / 1e12, "TFLOP/s", "mfma"
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     else:
-        hq, hkv = w.num_heads_q, w.num_heads_kv
-        byts = t_tok * hq * 64 * elem * 2 + t_tok * hq * 4 * 2  # pre: read O, dO, LSE; write D
+        byts = t_tok * hq * 64 * elem * 2 + t_tok * hq * 4 * 2  # read O, dO, LSE; write D
         work, unit, bound, peak = byts / 1e9, "GB/s", "hbm", PEAK_HBM_GBS
-    if w.dtype != "bf16" and unit == "TFLOP/s":
-        peak = PEAK_FP32_TFLOPS
     achieved = work / (per[dom] * 1e-3)
     roofline = dict(bound=bound, achieved=round(achieved, 3), peak=peak, unit=unit, frac=round(achieved / peak, 4),
                     traffic=read_traffic(args.workload, dom), kernel=dom, launch_ms=round(per[dom], 5))

@@ -110,9 +110,11 @@ size_t attn_sink_bwd_workspace_bytes(const attn_sink_shape* shape);
  * layout of q), dk/dv (dtype, layout of k) and dsinks (float32, [Hq]).
  * workspace: device memory of at least attn_sink_bwd_workspace_bytes(shape)
  * bytes, 256-byte aligned, owned by the caller, contents need not be initialised
- * and are garbage afterwards.  dk, dv and dq are accumulated with floating-point
- * atomics in the workspace, so their last bits can differ between runs; dsinks
- * is reduced in a fixed order and is bitwise reproducible. */
+ * and are garbage afterwards.  No atomics are used: dq is produced by one
+ * workgroup per query block, dk/dv by one per key block (summing the query heads
+ * of a kv head in a fixed order, through float32 partials in the workspace when
+ * the heads are split across workgroups), and dsinks by a fixed-order reduction,
+ * so every output is bitwise reproducible from run to run. */
 attn_sink_status attn_sink_bwd(const attn_sink_shape* shape,
                                const void* q, const void* k, const void* v,
                                const float* sinks,
