@@ -103,6 +103,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index (uniform)
   const int h = lane >> 5, c = lane & 31;
+  FragAddr<T> fa;
+  fa.init(lane);
   const int khi = f.causal ? clampi(qe - 1 + off + 1, 0, nk) : nk;
   const int klo = f.window > 0 ? clampi(qs + off - f.window + 1, 0, nk) : 0;
   const int qw = qs + 32 * w;
@@ -168,8 +170,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int s = 0; s < kD / KS; ++s) {
-        st[mt] = M::mma(lds_row_frag<T>(Ks, 32 * mt + c, KS * s + E * h), qf[s], st[mt]);
-        dpt[mt] = M::mma(lds_row_frag<T>(Vs, 32 * mt + c, KS * s + E * h), dof[s], dpt[mt]);
+        st[mt] = M::mma(fa.row(Ks, mt, s), qf[s], st[mt]);
+        dpt[mt] = M::mma(fa.row(Vs, mt, s), dof[s], dpt[mt]);
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -188,7 +190,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     for (int s = 0; s < C::BN / KS; ++s) {
       const typename M::Frag sf = pack_frag<T>(st, s);
 #pragma unroll
-      for (int md = 0; md < 2; ++md) dqt[md] = M::mma(lds_col_frag<T>(Ks, 32 * md, s, lane, true), sf, dqt[md]);
+      for (int md = 0; md < 2; ++md) dqt[md] = M::mma(fa.col(Ks, md, s), sf, dqt[md]);
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -281,6 +283,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index (uniform)
   const int h = lane >> 5, c = lane & 31;
+  FragAddr<T> fa;
+  fa.init(lane);
   const size_t kv_row = (size_t)f.hkv * kD, q_row = (size_t)f.hq * kD;
   const float sl2 = f.scale * kLog2e;
   const T* qhead_p = static_cast<const T*>(f.q) + (size_t)sq.start * q_row;
@@ -375,8 +379,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
         }
 #pragma unroll
         for (int s = 0; s < kD / KS; ++s) {
-          pt[mq] = M::mma(lds_row_frag<T>(Qs, 32 * mq + c, KS * s + E * h), kf[s], pt[mq]);
-          dst[mq] = M::mma(lds_row_frag<T>(dOs, 32 * mq + c, KS * s + E * h), vf[s], dst[mq]);
+          pt[mq] = M::mma(fa.row(Qs, mq, s), kf[s], pt[mq]);
+          dst[mq] = M::mma(fa.row(dOs, mq, s), vf[s], dst[mq]);
         }
       }
 #pragma unroll
@@ -405,8 +409,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
         const typename M::Frag sf = pack_frag<T>(dst, s);
 #pragma unroll
         for (int md = 0; md < 2; ++md) {
-          dvt[md] = M::mma(lds_col_frag<T>(dOs, 32 * md, s, lane, true), pf, dvt[md]);
-          dkt[md] = M::mma(lds_col_frag<T>(Qs, 32 * md, s, lane, true), sf, dkt[md]);
+          dvt[md] = M::mma(fa.col(dOs, md, s), pf, dvt[md]);
+          dkt[md] = M::mma(fa.col(Qs, md, s), sf, dkt[md]);
         }
       }
     };

@@ -13,10 +13,15 @@
 // k index through the permutation kc(f, h) below.
 //
 // LDS tiles are row-major with 64 columns.  bf16 tiles swizzle their 16-byte
-// chunks (chunk c of row r is stored at c ^ swz(r)) so that both access patterns
-// used on them are free of bank conflicts: eight consecutive rows read at the same
-// column (ds_read_b128), and four consecutive rows x 32 bytes read by a 16-lane
-// group (ds_read_b64_tr_b16).  fp32 tiles use a padded stride of 65 words.
+// chunks (chunk c of row r is stored at c ^ swz(r)).  The LDS has 64 four-byte
+// banks and serves a ds_read_b128 sixteen lanes per clock, so the sixteen rows a
+// 16-lane group reads at one logical chunk must land on sixteen distinct 16-byte
+// bank groups: a row pair (2j, 2j+1) spans all 64 banks, and swz must take eight
+// distinct values over the even (and over the odd) rows of any aligned 16 rows.
+// The transposing reads (ds_read_b64_tr_b16, four rows x 32 bytes per 16 lanes)
+// additionally want rows r and r+2 of an aligned quad in different halves of the
+// row: swz(r) = 4 * bit1(r) + bits2..3(r) satisfies both.  fp32 tiles use a padded
+// stride of 65 words.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -82,7 +87,7 @@ struct Tile;
 template <>
 struct Tile<bf16> {
   static constexpr int ELEMS_PER_ROW = 64;
-  __device__ static inline int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+  __device__ static inline int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
   // element offset of (row, col); col % 4 == 0 keeps a 4-element run inside one chunk
   __device__ static inline int off(int r, int c) { return r * 64 + ((((c >> 3) ^ swz(r)) << 3) | (c & 7)); }
 };
@@ -127,6 +132,81 @@ __device__ inline typename Mfma<T>::Frag lds_col_frag(const T* tile, int m0, int
     const int row = perm ? kc(s, h) : 2 * s + h;
     return tile[Tile<float>::off(row, m0 + (lane & 31))];
   }
+}
+
+// The same two fragment kinds through per-lane byte offsets computed once per
+// kernel.  Every fragment a kernel reads from a 64-column tile is one of eight
+// per-lane offsets plus a compile-time constant (the swizzle depends on row bits
+// 1..3 only, so moving by 16 or 32 rows keeps it), which lets a read of a tile at a
+// compile-time LDS address use the instruction's immediate offset and no address
+// arithmetic at all.  The offsets are pinned (opaque to the optimiser) so they are
+// kept in eight VGPRs rather than recomputed inside the loops.
+//   row(tile, mt, s): lds_row_frag(tile, 32*mt + c, KS*s + E*h)
+//   col(tile, md, s): lds_col_frag(tile, 32*md, s, lane, perm = true)
+template <typename T>
+struct FragAddr;
+
+template <>
+struct FragAddr<bf16> {
+  uint32_t row_[4];     // bytes of (row c, logical column 16 s + 8 h), s = 0..3
+  uint32_t col_[2][2];  // [j][md]: bytes of (row 8 j + 4 h + t/4, column 32 md + 16 (g&1) + 4 (t&3))
+  __device__ inline void init(int lane) {
+    const int h = lane >> 5, c = lane & 31, g = lane >> 4, t = lane & 15;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) row_[s] = 2u * (uint32_t)Tile<bf16>::off(c, 16 * s + 8 * h);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int md = 0; md < 2; ++md)
+        col_[j][md] = 2u * (uint32_t)Tile<bf16>::off(8 * j + 4 * h + (t >> 2), 32 * md + 16 * (g & 1) + 4 * (t & 3));
+#pragma unroll
+    for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(row_[s]));
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int md = 0; md < 2; ++md) asm volatile("" : "+v"(col_[j][md]));
+  }
+  __device__ inline bf16x8 row(const bf16* tile, int mt, int s) const {
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile) + row_[s] + mt * (32 * 64 * 2));
+  }
+  // rows kc(8 s, h) + t/4 = 16 s + 4 h + t/4 and kc(8 s + 4, h) + t/4 = that + 8
+  __device__ inline bf16x8 col(const bf16* tile, int md, int s) const {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const char* base = reinterpret_cast<const char*>(tile) + s * (16 * 64 * 2);
+    i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + col_[0][md]));
+    i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + col_[1][md]));
+    bf16x4 ab = __builtin_bit_cast(bf16x4, a), bb = __builtin_bit_cast(bf16x4, b);
+    return bf16x8{ab[0], ab[1], ab[2], ab[3], bb[0], bb[1], bb[2], bb[3]};
+  }
+};
+
+template <>
+struct FragAddr<float> {
+  int lane_;
+  __device__ inline void init(int lane) { lane_ = lane; }
+  __device__ inline float row(const float* tile, int mt, int s) const {
+    return lds_row_frag<float>(tile, 32 * mt + (lane_ & 31), 2 * s + (lane_ >> 5));
+  }
+  __device__ inline float col(const float* tile, int md, int s) const {
+    return lds_col_frag<float>(tile, 32 * md, s, lane_, true);
+  }
+};
+
+// acc += A B (bf16, 32x32x16) with the accumulator held in AGPRs.  Accumulators
+// that the vector ALUs never touch inside a loop (O, dQ, dK, dV) live there so the
+// MFMA's accumulator traffic does not compete with the VALU work of the other
+// wavefronts for the VGPR file.  Written as inline asm because the compiler,
+// told to keep the softmax tiles in VGPRs, would otherwise copy the accumulator
+// back and forth.  Hazards the compiler does not see through the asm: a VALU write
+// of A, B or the accumulator needs 2 wait states before the MFMA reads it (the
+// leading s_nop); the MFMA result needs agpr_fence() before any VALU reads it.
+// Back-to-back MFMAs on the same accumulator need none.
+__device__ inline void mma_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// 16 wait states: covers an MFMA result read by the vector ALUs (12 needed).
+__device__ inline void agpr_fence(f32x16& a0, f32x16& a1) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+a"(a0), "+a"(a1));
 }
 
 // Pack flat registers [E*s, E*s + E) of two stacked C tiles into an operand.

@@ -10,19 +10,21 @@
 // Design (FlashAttention-style single pass, one workgroup per 128 query rows of
 // one head; 4 wavefronts x 32 rows):
 //   * Q stays in registers as the B operand of S^T = K Q^T, so each lane owns one
-//     query row of S^T; row max / row sum are in-lane plus one lane-half swap.
+//     query row of S^T and all row reductions are in-lane (plus one lane-half swap).
 //   * K and V tiles of 64 keys are double-buffered row-major in LDS, loaded straight
 //     from HBM into LDS by buffer loads (swizzled so the operand reads are
 //     conflict-free); the V^T operand of O^T = V^T P^T is read with transposing LDS
-//     loads.
-//   * Online softmax in the exp2 domain (exp2(fma(s, scale*log2e, -m))).  The running
-//     max starts at the sink logit S_h*log2(e), not at -inf; the sink's own mass
-//     exp2(S_h*log2e - m) is added once at the end.  The running max is only raised
-//     (and O rescaled) when a row max exceeds it by more than 2^8, which after the
-//     first tiles almost never happens.  S_h = -inf is standard attention: the
-//     guarded max avoids exp2(-inf - -inf).
-//   * O^T = V^T P^T reuses the S^T accumulator registers as the B operand (P
-//     rounded to the element type), so P never leaves registers.
+//     loads.  Operand addresses are per-lane registers plus immediates.
+//   * Online softmax in the exp2 domain, P = exp2(fma(s, scale*log2e, -m)), with
+//     the running max m seeded by the sink logit S_h*log2(e); the sink's own mass
+//     exp2(S_h*log2e - m) is added once at the end.  m is not tracked per tile:
+//     it only has to keep every P below 2^64 (exact either way, since m cancels in
+//     O / l and lse = m + log2 l), so a tile is checked through the row sum it
+//     produces anyway, and only a tile whose sum breaks the bound (or is inf / NaN,
+//     as for S_h = -inf) takes the slow path: recompute its scores from the K tile
+//     still in LDS, raise m to their max, rescale O and l, redo the exponentials.
+//   * O^T = V^T P^T takes P (rounded to the element type) straight from the
+//     registers of S^T as its B operand.
 //   * Tiles outside the causal / sliding-window band are never visited; the mask
 //     is evaluated only on tiles that straddle a band edge or the sequence end.
 //   * Longest query tiles are dispatched first (causal load balance), and the
@@ -35,8 +37,10 @@
 
 namespace attn_sink {
 
-// Largest amount (log2 units) by which the running max may trail the row max.
-constexpr float kSlack = 8.f;
+// Bound on one lane's sum of exp2(x - m) over a key tile.  While every tile sum
+// stays below it no probability exceeds 2^64, so P and the fp32 sums O and l
+// cannot overflow for any realistic length and |v|.
+constexpr float kTileSumMax = 18446744073709551616.f;  // 2^64
 
 template <typename T>
 struct FwdCfg {
@@ -50,7 +54,9 @@ template <typename T>
 __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
   using C = FwdCfg<T>;
   using M = Mfma<T>;
+  using Frag = typename M::Frag;
   constexpr int E = M::E, KS = M::KS;
+  constexpr int NP = C::BN / KS;  // operand steps over the keys of a tile
   __shared__ __attribute__((aligned(16))) T smem[4 * C::TILE];  // [buf][K, V]
 
   const XcdSlot slot = xcd_slot(blockIdx.x, p.hkv, p.hq / p.hkv);
@@ -107,6 +113,8 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
   const int kt_begin = klo / C::BN;
   const int kt_end = khi > klo ? (khi + C::BN - 1) / C::BN : kt_begin;
 
+  FragAddr<T> fa;
+  fa.init(lane);
   TileLoader<T, C::BN, C::THREADS> kld, vld;
   kld.init(kbase_p, kv_row, nk, tid);
   vld.init(vbase_p, kv_row, nk, tid);
@@ -118,79 +126,88 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
   }
   __syncthreads();
 
-  // One tile: S^T, (mask), online softmax, O^T += V^T P^T.  FULL tiles need no mask;
-  // the masked instantiation selects per element without branches.  Both are
-  // straight-line code so the scheduler can overlap LDS reads, MFMA and exp.
-  auto body = [&](const T* Ks, const T* Vs, int kbase, auto full_tag) {
+  // S^T of one tile [64 keys x 32 queries], masked to -inf outside the band when
+  // the tile straddles a band edge.
+  auto scores = [&](f32x16* st, const T* Ks, int kbase, auto full_tag) __attribute__((always_inline)) {
     constexpr bool FULL = decltype(full_tag)::value;
-    f32x16 sacc[2];  // S^T tile [64 keys x 32 queries] as two 32x32 tiles
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.f;
+      for (int r = 0; r < 16; ++r) st[mt][r] = 0.f;
 #pragma unroll
-      for (int s = 0; s < kD / KS; ++s)
-        sacc[mt] = M::mma(lds_row_frag<T>(Ks, 32 * mt + c, KS * s + E * h), qf[s], sacc[mt]);
+      for (int s = 0; s < kD / KS; ++s) st[mt] = M::mma(fa.row(Ks, mt, s), qf[s], st[mt]);
     }
     if constexpr (!FULL) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          sacc[mt][r] =
-              visible(qi, kbase + 32 * mt + crow(r, h), off, nk, p.causal, p.window) ? sacc[mt][r] : -INFINITY;
+          st[mt][r] = visible(qi, kbase + 32 * mt + crow(r, h), off, nk, p.causal, p.window) ? st[mt][r] : -INFINITY;
     }
-    float mx = -INFINITY;
+  };
+  // P = exp2(s * sl2 + neg_m) in place, rounded into operands; returns the lane's
+  // sum of the rounded P (the values that multiply V).
+  auto probs = [&](f32x16* st, Frag* pf, float neg_m) __attribute__((always_inline)) -> float {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
-    mx = halves_max(mx) * sl2;
-    // Lazy rescale: the running max may trail the true max by up to kSlack (so
-    // probabilities stay <= 2^kSlack); O and l are rescaled only when some row of
-    // the wavefront exceeds that, which after the first tiles is rare.
-    if (__any(mx > m_run + kSlack)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);  // 0 when m_run = -inf
+      for (int r = 0; r < 16; ++r) st[mt][r] = fast_exp2(fmaf(st[mt][r], sl2, neg_m));
+    float sum = 0.f;
+#pragma unroll
+    for (int s = 0; s < NP; ++s) {
+      pf[s] = pack_frag<T>(st, s);
+      sum = frag_sum<T>(pf[s], sum);
+    }
+    return sum;
+  };
+
+  // One tile: S^T, (mask), P^T, O^T += V^T P^T.
+  auto body = [&](const T* Ks, const T* Vs, int kbase, auto full_tag) __attribute__((always_inline)) {
+    f32x16 st[2];
+    Frag pf[NP];
+    scores(st, Ks, kbase, full_tag);
+    float tsum = probs(st, pf, -m_run);  // m_run = -inf gives inf / NaN: caught below
+    if (__any(!(tsum <= kTileSumMax))) {
+      // Slow path (rare): raise the running max to this tile's row max.  The K
+      // tile is still in LDS, so the scores are simply computed again.
+      scores(st, Ks, kbase, full_tag);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[mt][r]);
+      const float m_new = fmaxf(m_run, halves_max(mx) * sl2);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);  // 0 when m_run = -inf
       l_run *= alpha;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
       m_run = m_new;
+      // m_new = -inf: every score of the row is masked so far, exp2(-inf + 0) = 0.
+      tsum = probs(st, pf, m_new == -INFINITY ? 0.f : -m_new);
     }
-    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+    l_run += tsum;
+    // O^T[d x q] += V^T[d x keys] . P^T[keys x q]
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int s = 0; s < NP; ++s)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[mt][r] = fast_exp2(fmaf(sacc[mt][r], sl2, neg_m));
-    // O^T[d x q] += V^T[d x keys] . P^T[keys x q]; the row sum is taken from the same
-    // rounded P that multiplies V.
-#pragma unroll
-    for (int s = 0; s < C::BN / KS; ++s) {
-      const typename M::Frag pf = pack_frag<T>(sacc, s);
-      l_run = frag_sum<T>(pf, l_run);
-#pragma unroll
-      for (int md = 0; md < 2; ++md) oacc[md] = M::mma(lds_col_frag<T>(Vs, 32 * md, s, lane, true), pf, oacc[md]);
-    }
+      for (int md = 0; md < 2; ++md) oacc[md] = M::mma(fa.col(Vs, md, s), pf[s], oacc[md]);
   };
-  // One pipeline step: prefetch tile kt+1 into registers, compute tile kt from LDS,
-  // commit the prefetched tile to the other buffer, barrier.
-  auto step = [&](int kt, auto full_tag) {
+  // One pipeline step: start loading tile kt+1 into the other buffer, compute tile
+  // kt, wait for the load, barrier.  `cur` / `nxt` are the two buffers (K then V).
+  auto step = [&](int kt, T* cur, T* nxt, auto full_tag) __attribute__((always_inline)) {
     constexpr bool FULL = decltype(full_tag)::value;
-    const int buf = (kt - kt_begin) & 1;
     const bool more = kt + 1 < kt_end;
-    T* nb = smem + (buf ^ 1) * 2 * C::TILE;  // read in the previous step, before its barrier
-    if (more) {
-      kld.issue((kt + 1) * C::BN, nb);
-      vld.issue((kt + 1) * C::BN, nb + C::TILE);
+    if (more) {  // nxt was last read in the previous step, before its barrier
+      kld.issue((kt + 1) * C::BN, nxt);
+      vld.issue((kt + 1) * C::BN, nxt + C::TILE);
     }
     const int kbase = kt * C::BN;
-    const T* Ks = smem + buf * 2 * C::TILE;
     if constexpr (FULL) {
-      body(Ks, Ks + C::TILE, kbase, full_tag);
+      body(cur, cur + C::TILE, kbase, full_tag);
     } else {
-      if (kbase < whi && kbase + C::BN > wlo) body(Ks, Ks + C::TILE, kbase, full_tag);
+      if (kbase < whi && kbase + C::BN > wlo) body(cur, cur + C::TILE, kbase, full_tag);
     }
     if (more) {
       kld.finish();
@@ -198,9 +215,17 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
     }
     __syncthreads();
   };
+  T* const buf0 = smem;
+  T* const buf1 = smem + 2 * C::TILE;
+  auto masked_step = [&](int kt) __attribute__((always_inline)) {
+    const bool odd = (kt - kt_begin) & 1;
+    step(kt, odd ? buf1 : buf0, odd ? buf0 : buf1, std::false_type{});
+  };
   // Tiles [wf_lo, wf_hi) are fully visible to every row of this wavefront: inside
   // the window's left edge, left of the diagonal and inside the sequence.  Every
-  // wavefront runs the same number of steps (one barrier each), only the body differs.
+  // wavefront runs the same number of steps (one barrier each), only the body
+  // differs.  The unmasked tiles run in pairs so both buffer addresses are
+  // compile-time constants there.
   int wf_lo = kt_begin, wf_hi = kt_begin;
   if (wave_rows) {
     const int lo_key = p.window > 0 ? qw_end + off - p.window : 0;  // first key every row sees from the left
@@ -209,9 +234,20 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
     wf_hi = clampi(hi_key > 0 ? hi_key / C::BN : 0, wf_lo, kt_end);
   }
   int kt = kt_begin;
-  for (; kt < wf_lo; ++kt) step(kt, std::false_type{});
-  for (; kt < wf_hi; ++kt) step(kt, std::true_type{});
-  for (; kt < kt_end; ++kt) step(kt, std::false_type{});
+  for (; kt < wf_lo; ++kt) masked_step(kt);
+  if (kt < wf_hi && ((kt - kt_begin) & 1)) {
+    step(kt, buf1, buf0, std::true_type{});
+    ++kt;
+  }
+  for (; kt + 1 < wf_hi; kt += 2) {
+    step(kt, buf0, buf1, std::true_type{});
+    step(kt + 1, buf1, buf0, std::true_type{});
+  }
+  if (kt < wf_hi) {
+    step(kt, buf0, buf1, std::true_type{});
+    ++kt;
+  }
+  for (; kt < kt_end; ++kt) masked_step(kt);
 
   // ---- epilogue: add the sink's mass once, normalise, write O and LSE.
   const float m_use = m_run == -INFINITY ? 0.f : m_run;

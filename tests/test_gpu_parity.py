@@ -157,14 +157,30 @@ def test_gqa_equals_duplicated_kv(gpu_lib):
 
 
 def test_repeatability(gpu_lib):
-    """Forward and the sink gradient are bitwise repeatable; dq/dk/dv use float atomics."""
+    """Every output is bitwise repeatable (no atomics; fixed reduction orders)."""
     inp = random_case([700, 333], 8, 2, 64, "bf16", seed=17)
     runs = [gpu_fwd_bwd(gpu_lib, inp) for _ in range(3)]
     for r in runs[1:]:
-        for key in ("o", "lse", "dsinks"):
+        for key in ALL:
             assert np.array_equal(r[key], runs[0][key]), key
-        for key in ("dq", "dk", "dv"):
-            assert np.max(np.abs(r[key] - runs[0][key])) <= 1e-2 * np.max(np.abs(runs[0][key])), key
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_running_max_raised_mid_row(gpu_lib, dtype):
+    """Key norms ramp up 40x along the sequence, so the scores of a row grow by far
+    more than 64 (log2 units) from its first key tiles to its last: the forward must
+    raise its running max and rescale O several times within one row.
+
+    Tolerance: scores reach |s| ~ 150 here, and a float32 score carries an absolute
+    error of about |s| * 2^-24 * sqrt(64) ~ 7e-5, which is the relative error it
+    puts into exp(s); float32 is therefore held to 2e-4 instead of 1e-5 (bf16, whose
+    bar comes from rounding P to 8 bits, keeps its usual one)."""
+    inp = random_case([700, 190], 4, 2, 64, dtype, seed=21)
+    ramp = torch.cat([torch.linspace(1.0, 40.0, 700), torch.linspace(1.0, 40.0, 190)])
+    inp["k"] = (inp["k"].float() * ramp[:, None, None]).to(inp["k"].dtype)
+    s_max = float((inp["q"].float() @ inp["k"].float().reshape(-1, 64).T).abs().max()) * 0.125
+    print(f"[case] growing scores {dtype}: max |s| = {s_max:.1f}", flush=True)
+    _full_case(gpu_lib, inp, f"growing scores {dtype}", tol=2e-4 if dtype == "fp32" else None)
 
 
 def test_autograd_wrapper(gpu_lib):
