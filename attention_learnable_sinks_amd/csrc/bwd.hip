@@ -134,6 +134,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const float lse2 = qok ? f.lse[(size_t)head * f.total_q + sq.start + qi] * kLog2e : 0.f;
   const float dd = qok ? a.delta[(size_t)head * f.total_q + sq.start + qi] : 0.f;
   const float sl2 = f.scale * kLog2e;
+  f32x16 neg_dd;  // -D of the lane's row in every register
+#pragma unroll
+  for (int r = 0; r < 16; ++r) neg_dd[r] = -dd;
 
   f32x16 dqt[2];  // dQ^T [64 d x 32 q]
 #pragma unroll
@@ -171,7 +174,12 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int s = 0; s < kD / KS; ++s) {
         st[mt] = M::mma(fa.row(Ks, mt, s), qf[s], st[mt]);
-        dpt[mt] = M::mma(fa.row(Vs, mt, s), dof[s], dpt[mt]);
+        if constexpr (sizeof(T) == 2) {
+          // bf16: dP^T starts from -D (a loop-invariant seed), so it ends at dP^T - D.
+          dpt[mt] = s == 0 ? mma_seeded(fa.row(Vs, mt, s), dof[s], neg_dd) : M::mma(fa.row(Vs, mt, s), dof[s], dpt[mt]);
+        } else {
+          dpt[mt] = M::mma(fa.row(Vs, mt, s), dof[s], dpt[mt]);
+        }
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -182,7 +190,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
         float pv = fast_exp2(fmaf(st[mt][r], sl2, -lse2));  // P^T
         if constexpr (!FULL)
           pv = (qok & visible(qi, kbase + 32 * mt + crow(r, h), off, nk, f.causal, f.window)) ? pv : 0.f;
-        st[mt][r] = pv * (dpt[mt][r] - dd);  // dS^T
+        st[mt][r] = pv * (sizeof(T) == 2 ? dpt[mt][r] : dpt[mt][r] - dd);  // dS^T = P^T (dP^T - D)
       }
     // dQ^T[d x q] += K^T[d x keys] . dS^T[keys x q]
     __builtin_amdgcn_s_setprio(1);
@@ -355,7 +363,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
       dold.finish();
       if (tid < C::BMB) {
         lse2_s[buf][tid] = lse_r;
-        dd_s[buf][tid] = dd_r;
+        dd_s[buf][tid] = sizeof(T) == 2 ? -dd_r : dd_r;  // bf16: negated, it seeds dP
       }
     };
 
@@ -377,10 +385,22 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
           pt[mq][r] = 0.f;
           dst[mq][r] = 0.f;
         }
+        f32x16 seed;  // bf16: -D of each register's query row; dP then ends at dP - D
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dd_s[buf][32 * mq + crow(4 * r4, h)]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) seed[4 * r4 + e] = d4[e];
+          }
+        }
 #pragma unroll
         for (int s = 0; s < kD / KS; ++s) {
           pt[mq] = M::mma(fa.row(Qs, mq, s), kf[s], pt[mq]);
-          dst[mq] = M::mma(fa.row(dOs, mq, s), vf[s], dst[mq]);
+          if constexpr (sizeof(T) == 2)
+            dst[mq] = s == 0 ? mma_seeded(fa.row(dOs, mq, s), vf[s], seed) : M::mma(fa.row(dOs, mq, s), vf[s], dst[mq]);
+          else
+            dst[mq] = M::mma(fa.row(dOs, mq, s), vf[s], dst[mq]);
         }
       }
 #pragma unroll
@@ -389,7 +409,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
         for (int r4 = 0; r4 < 4; ++r4) {
           const int ql = 32 * mq + crow(4 * r4, h);  // 4 consecutive query rows
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2_s[buf][ql]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dd_s[buf][ql]);
+          f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (sizeof(T) != 2) d4 = *reinterpret_cast<const f32x4*>(&dd_s[buf][ql]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * r4 + e;
@@ -399,7 +420,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
               pv = ((qi < nq) & visible(qi, kj, off, nk, f.causal, f.window)) ? pv : 0.f;
             }
             pt[mq][r] = pv;
-            dst[mq][r] = pv * (dst[mq][r] - d4[e]);
+            dst[mq][r] = pv * (sizeof(T) == 2 ? dst[mq][r] : dst[mq][r] - d4[e]);  // dS = P (dP - D)
           }
         }
       // dV^T[d x keys] += dO^T[d x q] P[q x keys];  dK^T += Q^T dS

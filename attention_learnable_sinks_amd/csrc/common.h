@@ -204,6 +204,18 @@ struct FragAddr<float> {
 __device__ inline void mma_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+// d = A B + c (bf16, 32x32x16) with c in registers distinct from d: the first
+// step of an accumulation that starts from a non-zero seed kept elsewhere (the
+// compiler would first copy the seed into d).  The leading s_nop covers a VALU
+// write of A, B or c just before.  MFMAs that go on accumulating into d need no
+// wait states; a VALU read of d must come after a later compiler-emitted MFMA
+// (or after agpr_fence-like padding).
+__device__ inline f32x16 mma_seeded(bf16x8 a, bf16x8 b, const f32x16& c) {
+  f32x16 d;
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
 // 16 wait states: covers an MFMA result read by the vector ALUs (12 needed).
 __device__ inline void agpr_fence(f32x16& a0, f32x16& a1) {
   asm volatile("s_nop 7\n\ts_nop 7" : "+a"(a0), "+a"(a1));
