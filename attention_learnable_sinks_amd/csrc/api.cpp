@@ -160,7 +160,7 @@ attn_sink_status attn_sink_bwd(const attn_sink_shape* shape, const void* q, cons
   a.dv = dv;
   a.dsinks = dsinks;
   char* base = static_cast<char*>(workspace);
-  a.delta = reinterpret_cast<float*>(base + ws.delta);
+  a.rowstat = reinterpret_cast<float*>(base + ws.rowstat);
   a.dsink_part = reinterpret_cast<float*>(base + ws.dsink_part);
   a.dk_part = reinterpret_cast<float*>(base + ws.dk_part);
   a.dv_part = reinterpret_cast<float*>(base + ws.dv_part);

@@ -29,6 +29,7 @@
 //                  workgroups (to fill the GPU), each split writes an fp32 partial.
 //   4. bwd_finish: fixed-order sums of the dS_h partials and of the dK/dV partials.
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "kernels.h"
@@ -56,8 +57,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
     acc += __shfl_xor(acc, 1);
     acc += __shfl_xor(acc, 2);
     if (part == 0) {
-      a.delta[(size_t)head * f.total_q + row] = acc;
       const float lse = f.lse[(size_t)head * f.total_q + row];
+      a.rowstat[(size_t)(2 * head) * f.total_q + row] = lse * kLog2e;
+      a.rowstat[(size_t)(2 * head + 1) * f.total_q + row] = -acc;
       const float sink = f.sinks[head];
       const float ps = (lse > -INFINITY && sink > -INFINITY) ? fast_exp2((sink - lse) * kLog2e) : 0.f;
       contrib = -ps * acc;
@@ -131,8 +133,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
       dof[s] = global_frag<T>(dsrc + KS * s + E * h, qok);
     }
   }
-  const float lse2 = qok ? f.lse[(size_t)head * f.total_q + sq.start + qi] * kLog2e : 0.f;
-  const float dd = qok ? a.delta[(size_t)head * f.total_q + sq.start + qi] : 0.f;
+  const float lse2 = qok ? a.rowstat[(size_t)(2 * head) * f.total_q + sq.start + qi] : 0.f;
+  const float dd = qok ? -a.rowstat[(size_t)(2 * head + 1) * f.total_q + sq.start + qi] : 0.f;
   const float sl2 = f.scale * kLog2e;
   f32x16 neg_dd;  // -D of the lane's row in every register
 #pragma unroll
@@ -155,6 +157,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     kld.finish();
     vld.finish();
   }
+  vmem_drain();
   __syncthreads();
 
   // One tile: S^T, dP^T, P^T, dS^T, dQ^T += K^T dS^T; FULL tiles need no mask.
@@ -339,7 +342,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
       }
 
     TileLoader<T, C::BMB, C::THREADS> qld, dold;
-    float lse_r = 0.f, dd_r = 0.f;
+    RowLoader lld, dld;  // the tile's lse * log2(e) and -D rows (waves 0 and 1)
     int staged_head = -1;
     // Start moving (head, query tile) of iteration `it` into LDS buffer `buf`.
     auto stage = [&](int it, int buf) __device__ {
@@ -348,29 +351,28 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
       if (hd != staged_head) {  // uniform: new descriptors when the query head changes
         qld.init(qhead_p + hd * kD, q_row, nq, tid);
         dold.init(dohead_p + hd * kD, q_row, nq, tid);
+        lld.init(a.rowstat + (size_t)(2 * hd) * f.total_q + sq.start, nq);
+        dld.init(a.rowstat + (size_t)(2 * hd + 1) * f.total_q + sq.start, nq);
         staged_head = hd;
       }
       qld.issue(qt * C::BMB, smem + buf * 2 * C::TILE);
       dold.issue(qt * C::BMB, smem + buf * 2 * C::TILE + C::TILE);
-      if (tid < C::BMB) {
-        const int qi = qt * C::BMB + tid;
-        lse_r = qi < nq ? f.lse[(size_t)hd * f.total_q + sq.start + qi] * kLog2e : 0.f;
-        dd_r = qi < nq ? a.delta[(size_t)hd * f.total_q + sq.start + qi] : 0.f;
-      }
+      // The row statistics go straight to LDS as well (rows past the sequence read
+      // as 0), so no load in the loop writes a register the loop has to wait for.
+      if (w == 0) lld.issue(qt * C::BMB, lse2_s[buf], lane);
+      if (w == 1) dld.issue(qt * C::BMB, dd_s[buf], lane);
     };
     auto commit = [&](int buf) __device__ {
       qld.finish();
-      dold.finish();
-      if (tid < C::BMB) {
-        lse2_s[buf][tid] = lse_r;
-        dd_s[buf][tid] = sizeof(T) == 2 ? -dd_r : dd_r;  // bf16: negated, it seeds dP
-      }
+      dold.finish();  // also covers the row loads (same counter)
+      (void)buf;
     };
 
     if (n_it > 0) {
       stage(0, 0);
       commit(0);
     }
+    vmem_drain();
     __syncthreads();
     // One (head, query tile): S, dP, P, dS, dV^T += dO^T P, dK^T += Q^T dS.
     auto body = [&](int buf, int qbase, auto full_tag) __device__ {
@@ -385,7 +387,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
           pt[mq][r] = 0.f;
           dst[mq][r] = 0.f;
         }
-        f32x16 seed;  // bf16: -D of each register's query row; dP then ends at dP - D
+        f32x16 seed;  // bf16: -D of each register's query row (dd_s holds -D); dP then ends at dP - D
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
@@ -394,13 +396,23 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
             for (int e = 0; e < 4; ++e) seed[4 * r4 + e] = d4[e];
           }
         }
+        // All operands of this block's 8 MFMAs are read first; the scheduling barrier
+        // keeps the reads from being sunk next to their MFMAs (which would expose the
+        // LDS latency once per MFMA).
+        typename M::Frag qa[kD / KS], da[kD / KS];
 #pragma unroll
         for (int s = 0; s < kD / KS; ++s) {
-          pt[mq] = M::mma(fa.row(Qs, mq, s), kf[s], pt[mq]);
+          qa[s] = fa.row(Qs, mq, s);
+          da[s] = fa.row(dOs, mq, s);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < kD / KS; ++s) {
+          pt[mq] = M::mma(qa[s], kf[s], pt[mq]);
           if constexpr (sizeof(T) == 2)
-            dst[mq] = s == 0 ? mma_seeded(fa.row(dOs, mq, s), vf[s], seed) : M::mma(fa.row(dOs, mq, s), vf[s], dst[mq]);
+            dst[mq] = s == 0 ? mma_seeded(da[s], vf[s], seed) : M::mma(da[s], vf[s], dst[mq]);
           else
-            dst[mq] = M::mma(fa.row(dOs, mq, s), vf[s], dst[mq]);
+            dst[mq] = M::mma(da[s], vf[s], dst[mq]);
         }
       }
 #pragma unroll
@@ -420,7 +432,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
               pv = ((qi < nq) & visible(qi, kj, off, nk, f.causal, f.window)) ? pv : 0.f;
             }
             pt[mq][r] = pv;
-            dst[mq][r] = pv * (sizeof(T) == 2 ? dst[mq][r] : dst[mq][r] - d4[e]);  // dS = P (dP - D)
+            dst[mq][r] = pv * (sizeof(T) == 2 ? dst[mq][r] : dst[mq][r] + d4[e]);  // dS = P (dP - D); d4 = -D
           }
         }
       // dV^T[d x keys] += dO^T[d x q] P[q x keys];  dK^T += Q^T dS
@@ -548,7 +560,7 @@ BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k) {
   w.pre_blocks = (rows + kPreRows - 1) / kPreRows;
   w.splits = bwd_head_splits(hq, hkv, total_k);
   size_t o = 0;
-  w.delta = o;       o = align256(o + (size_t)hq * total_q * 4);
+  w.rowstat = o;     o = align256(o + (size_t)hq * 2 * total_q * 4);
   w.dsink_part = o;  o = align256(o + (size_t)hq * w.pre_blocks * 4);
   const size_t part = w.splits > 1 ? (size_t)w.splits * total_k * hkv * kD * 4 : 0;
   w.dk_part = o;     o = align256(o + part);

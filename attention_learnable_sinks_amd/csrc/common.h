@@ -209,10 +209,11 @@ __device__ inline void mma_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
 // compiler would first copy the seed into d).  The leading s_nop covers a VALU
 // write of A, B or c just before.  MFMAs that go on accumulating into d need no
 // wait states; a VALU read of d must come after a later compiler-emitted MFMA
-// (or after agpr_fence-like padding).
+// (or after agpr_fence-like padding).  Not volatile: a volatile asm would be a
+// scheduling boundary and pin the LDS operand reads around it.
 __device__ inline f32x16 mma_seeded(bf16x8 a, bf16x8 b, const f32x16& c) {
   f32x16 d;
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "v"(b), "v"(c));
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "v"(b), "v"(c));
   return d;
 }
 
@@ -311,6 +312,31 @@ struct Stager {
   }
 };
 
+// Buffer load whose data goes straight to LDS: lane i's bytes land at LDS byte
+// address lds + size * i.  Issued through inline asm on purpose: the compiler
+// tracks its own LDS DMA builtin as an LDS write it cannot disambiguate from the
+// transposing LDS reads, and then waits for every outstanding DMA (the prefetch
+// of the next tile) before the first such read of the current tile.  The caller
+// orders the DMA explicitly (s_waitcnt vmcnt(0) + barrier before the data is
+// read), and the compiler's own vmcnt waits stay correct (only more conservative)
+// because vector-memory loads retire in order.
+__device__ inline uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ inline void lds_dma_b128(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds) : "memory");
+}
+__device__ inline void lds_dma_b32(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("buffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds) : "memory");
+}
+
+// Wait for every outstanding vector-memory load.  Called once after a kernel's
+// prologue (whose waits are conditional): it tells the compiler that the register
+// loads issued so far (fragments kept in registers for the whole loop) are done,
+// so it places no vmcnt wait for them inside the loop, where it would also wait
+// for the asm tile DMAs in flight.
+__device__ inline void vmem_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
 // Tile loader with one interface for both element types: issue(row0, tile) starts
 // moving rows [row0, row0 + ROWS) of the head into LDS tile `tile`, finish() makes
 // sure they have arrived (the caller then synchronises the workgroup).
@@ -345,12 +371,9 @@ struct TileLoader<bf16, ROWS, THREADS> {
   }
   __device__ inline void issue(int row0, bf16* tile) {
     const uint32_t soff = (uint32_t)row0 * row_bytes;
-#if defined(__HIP_DEVICE_COMPILE__)  // the host pass of templated kernels must not see this builtin
-    typedef __attribute__((address_space(3))) void lds_void;
+#if defined(__HIP_DEVICE_COMPILE__)  // device-only asm
 #pragma unroll
-    for (int n = 0; n < N; ++n)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + (first_slot + n * 64) * 8), 16, voff[n], soff,
-                                               0, 0);
+    for (int n = 0; n < N; ++n) lds_dma_b128(rsrc, voff[n], soff, lds_address(tile + (first_slot + n * 64) * 8));
 #endif
   }
   __device__ inline void finish() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
@@ -370,6 +393,21 @@ struct TileLoader<float, ROWS, THREADS> {
     dst = tile;
   }
   __device__ inline void finish() { st.store(dst, tid_); }
+};
+
+// 64 consecutive floats of one row-statistics array moved straight into LDS by one
+// wavefront instruction (lane i -> float i); rows past `nrows` read as zero.
+struct RowLoader {
+  __amdgpu_buffer_rsrc_t rsrc;
+  __device__ inline void init(const float* base, int nrows) {
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, nrows * 4, kBufferWord3);
+  }
+  // Call from one whole wavefront; finish with the tile loads' wait (vmcnt(0)).
+  __device__ inline void issue(int row0, float* lds, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    lds_dma_b32(rsrc, (uint32_t)lane * 4u, (uint32_t)row0 * 4u, lds_address(lds));
+#endif
+  }
 };
 
 // ---------------------------------------------------------------- misc

@@ -124,6 +124,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
     kld.finish();
     vld.finish();
   }
+  vmem_drain();
   __syncthreads();
 
   // S^T of one tile [64 keys x 32 queries], masked to -inf outside the band when

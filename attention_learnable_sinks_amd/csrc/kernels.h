@@ -30,7 +30,7 @@ struct BwdArgs {
   void* dv;
   float* dsinks;
   // workspace carve-up (float32, device)
-  float* delta;       // [hq, total_q]   D_i = <dO_i, O_i>
+  float* rowstat;     // [hq, 2, total_q]: lse_i * log2(e), then -D_i with D_i = <dO_i, O_i>
   float* dsink_part;  // [hq, pre_blocks]
   float* dk_part;     // [splits, total_k, hkv, 64] (only when splits > 1)
   float* dv_part;     // [splits, total_k, hkv, 64] (only when splits > 1)
@@ -44,7 +44,7 @@ const char* kernel_name(int id);
 
 // Workspace layout for a backward call; offsets in bytes from the workspace base.
 struct BwdWorkspace {
-  size_t delta, dsink_part, dk_part, dv_part, total;
+  size_t rowstat, dsink_part, dk_part, dv_part, total;
   int pre_blocks, splits;
 };
 BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k);
