@@ -543,22 +543,35 @@ __global__ __launch_bounds__(256) void bwd_finish_kernel(BwdArgs a) {
 // ----------------------------------------------------------------------------- launchers
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int bwd_head_splits(int hq, int hkv, int total_k) {
-  // About total_k / 256 folded pairs of 128-key tiles per kv head; split the GQA
-  // group over more workgroups until there are at least two per CU.
+int bwd_head_splits(int hq, int hkv, int total_k, int num_seqs) {
+  // The dK/dV grid has one workgroup per (sequence, kv head, head split, folded pair
+  // of 128-key tiles), all of about the same work for one sequence length, and
+  // about 512 of them run at once (256 CUs x 2).  Splitting the query heads of a
+  // kv head over s workgroups divides the work per workgroup by s, so the time
+  // goes as ceil(workgroups / 512) / s: pick the s that minimises it (the fewest
+  // splits on a tie, as every split adds float32 partials to reduce).
   const int group = hq / hkv;
-  long long pairs = (total_k + 255) / 256;
+  long long pairs = (total_k + 255) / 256 + num_seqs / 2;  // folded pairs over all sequences (approx.)
   if (pairs < 1) pairs = 1;
-  int s = 1;
-  while (s < group && group % (2 * s) == 0 && pairs * hkv * s < 512) s *= 2;
-  return s;
+  constexpr long long kConcurrent = 512;
+  int best = 1;
+  long long best_num = 0, best_den = 1;  // cost = rounds / s as a fraction
+  for (int sp = 1; sp <= group && group % sp == 0; sp *= 2) {
+    const long long rounds = (pairs * hkv * sp + kConcurrent - 1) / kConcurrent;
+    if (sp == 1 || rounds * best_den < best_num * sp) {
+      best = sp;
+      best_num = rounds;
+      best_den = sp;
+    }
+  }
+  return best;
 }
 
-BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k) {
+BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k, int num_seqs) {
   BwdWorkspace w;
   const int rows = total_q > 0 ? total_q : 1;
   w.pre_blocks = (rows + kPreRows - 1) / kPreRows;
-  w.splits = bwd_head_splits(hq, hkv, total_k);
+  w.splits = bwd_head_splits(hq, hkv, total_k, num_seqs);
   size_t o = 0;
   w.rowstat = o;     o = align256(o + (size_t)hq * 2 * total_q * 4);
   w.dsink_part = o;  o = align256(o + (size_t)hq * w.pre_blocks * 4);

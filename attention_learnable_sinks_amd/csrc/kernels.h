@@ -47,8 +47,8 @@ struct BwdWorkspace {
   size_t rowstat, dsink_part, dk_part, dv_part, total;
   int pre_blocks, splits;
 };
-BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k);
-int bwd_head_splits(int hq, int hkv, int total_k);
+BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k, int num_seqs);
+int bwd_head_splits(int hq, int hkv, int total_k, int num_seqs);
 
 // Each launcher enqueues one kernel on `stream` and returns hipGetLastError().
 hipError_t launch_fwd(const FwdArgs& a, int fp32, hipStream_t stream);
