@@ -275,9 +275,13 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
   using M = Mfma<T>;
   constexpr int E = M::E, KS = M::KS;
   const FwdArgs& f = a.f;
-  __shared__ __attribute__((aligned(16))) T smem[4 * C::TILE];  // [buf][Q, dO]
-  __shared__ __attribute__((aligned(16))) float lse2_s[2][C::BMB];
-  __shared__ __attribute__((aligned(16))) float dd_s[2][C::BMB];
+  // bf16 stages tiles two steps ahead (three buffers); fp32 stages through registers, one ahead.
+  constexpr int NB = sizeof(T) == 2 ? 3 : 2;
+  static_assert(sizeof(T) != 2 || TileLoader<bf16, C::BMB, C::THREADS>::N == 2,
+                "the vmcnt counts in step() assume two DMA instructions per tile and wavefront");
+  __shared__ __attribute__((aligned(16))) T smem[NB * 2 * C::TILE];  // [buf][Q, dO]
+  __shared__ __attribute__((aligned(16))) float lse2_s[NB][C::BMB];
+  __shared__ __attribute__((aligned(16))) float dd_s[NB][C::BMB];
 
   const XcdSlot slot = xcd_slot(blockIdx.x, f.hkv, a.splits);
   const int b = slot.seq, g = slot.kv, split = slot.item;
@@ -370,7 +374,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
 
     if (n_it > 0) {
       stage(0, 0);
-      commit(0);
+      if constexpr (NB == 3) {
+        if (n_it > 1) stage(1, 1);
+      } else {
+        commit(0);
+      }
     }
     vmem_drain();
     __syncthreads();
@@ -449,9 +457,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
     };
     auto step = [&](int it, int qt, auto full_tag) __device__ {
       constexpr bool FULL = decltype(full_tag)::value;
-      const int buf = it & 1;
-      const bool more = it + 1 < n_it;
-      if (more) stage(it + 1, buf ^ 1);  // that buffer was read in the previous step
+      const int buf = it % NB;
+      // bf16: tile it+2 goes to the buffer read in the previous step; fp32: tile it+1.
+      const bool more = it + NB - 1 < n_it;
+      if (more) stage(it + NB - 1, (it + NB - 1) % NB);
       const int qbase = qt * C::BMB;
       if constexpr (FULL) {
         body(buf, qbase, full_tag);
@@ -459,7 +468,20 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
         const int qlast = min(qbase + C::BMB, nq) - 1;
         if (wave_keys && qbase < wqhi && qlast >= wqlo) body(buf, qbase, full_tag);
       }
-      if (more) commit(buf ^ 1);
+      if constexpr (NB == 3) {
+        // Tile it+1 must have landed; tile it+2's DMAs (this wavefront's last 4 or 5
+        // vector-memory instructions, the lse / -D row on waves 0 and 1) may still fly.
+        if (more) {
+          if (w < 2)
+            __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5)
+          else
+            __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+        } else {
+          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        }
+      } else {
+        if (more) commit((it + 1) % NB);
+      }
       __syncthreads();
     };
     // Query tiles [qf_lo, qf_hi) are fully visible to all 32 keys of this wavefront:
