@@ -122,6 +122,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   // Q and dO fragments (B operands of S^T = K Q^T and dP^T = V dO^T); lse and D of the lane's row.
   const int qi = qw + c;
   const bool qok = qi < nq;
+  Span row_keys = keys_of_row(qi, off, nk, f.causal, f.window);  // the keys row qi sees
+  if (!qok) row_keys.len = 0u;
   typename M::Frag qf[kD / KS], dof[kD / KS];
   {
     const size_t o = ((size_t)(sq.start + (qok ? qi : 0)) * f.hq + head) * kD;
@@ -191,8 +193,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float pv = fast_exp2(fmaf(st[mt][r], sl2, -lse2));  // P^T
-        if constexpr (!FULL)
-          pv = (qok & visible(qi, kbase + 32 * mt + crow(r, h), off, nk, f.causal, f.window)) ? pv : 0.f;
+        if constexpr (!FULL)  // key kbase + 4h + (32 mt + 8 (r/4) + r%4)
+          pv = in_span(kbase + 4 * h + 32 * mt + 8 * (r / 4) + r % 4, row_keys) ? pv : 0.f;
         st[mt][r] = pv * (sizeof(T) == 2 ? dpt[mt][r] : dpt[mt][r] - dd);  // dS^T = P^T (dP^T - D)
       }
     // dQ^T[d x q] += K^T[d x keys] . dS^T[keys x q]
@@ -325,6 +327,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
     // K and V fragments (B operands of S = Q K^T and dP = dO V^T): lane owns key kj.
     const int kj = kw + c;
     const bool kok = kj < nk;
+    const Span key_rows = rows_of_key(kj, off, nq, nk, f.causal, f.window);  // the rows that see key kj
     typename M::Frag kf[kD / KS], vf[kD / KS];
     {
       const size_t o = (size_t)(sk.start + (kok ? kj : 0)) * kv_row + g * kD;
@@ -436,8 +439,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
             const int r = 4 * r4 + e;
             float pv = fast_exp2(fmaf(pt[mq][r], sl2, -l4[e]));
             if constexpr (!FULL) {
-              const int qi = qbase + ql + e;
-              pv = ((qi < nq) & visible(qi, kj, off, nk, f.causal, f.window)) ? pv : 0.f;
+              // query qbase + 4h + (32 mq + 8 r4 + e), a constant per element
+              pv = in_span(qbase + 4 * h + 32 * mq + 8 * r4 + e, key_rows) ? pv : 0.f;
             }
             pt[mq][r] = pv;
             dst[mq][r] = pv * (sizeof(T) == 2 ? dst[mq][r] : dst[mq][r] + d4[e]);  // dS = P (dP - D); d4 = -D

@@ -428,6 +428,26 @@ __device__ inline bool visible(int i, int j, int off, int nk, int causal, int wi
   return (j < nk) & ((causal == 0) | (j <= i + off)) & ((window <= 0) | (j > i + off - window));
 }
 
+// The keys query row i sees form one interval, and so do the query rows that see
+// key j (causal limit, window limit and sequence ends folded together).  A masked
+// tile then costs one unsigned range check per element: (x - lo) < len.
+struct Span {
+  int lo;
+  unsigned len;
+};
+__device__ inline Span keys_of_row(int i, int off, int nk, int causal, int window) {
+  const int hi = causal ? min(i + off + 1, nk) : nk;      // key <= i + off, key < nk
+  const int lo = window > 0 ? max(i + off - window + 1, 0) : 0;  // key > i + off - window
+  return {lo, (unsigned)max(hi - lo, 0)};
+}
+__device__ inline Span rows_of_key(int j, int off, int nq, int nk, int causal, int window) {
+  if (j >= nk) return {0, 0u};
+  const int lo = causal ? max(j - off, 0) : 0;                   // i >= j - off
+  const int hi = window > 0 ? min(j - off + window, nq) : nq;    // i < j - off + window, i < nq
+  return {lo, (unsigned)max(hi - lo, 0)};
+}
+__device__ inline bool in_span(int x, Span s) { return (unsigned)(x - s.lo) < s.len; }
+
 // Workgroups are dealt to the 8 XCDs round-robin (XCD = linear index % 8).  These
 // maps turn the linear index of the workgroup's first grid dimension into
 // (sequence, kv head, item within that kv head) such that every workgroup of kv

@@ -113,6 +113,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
   const int kt_begin = klo / C::BN;
   const int kt_end = khi > klo ? (khi + C::BN - 1) / C::BN : kt_begin;
 
+  const Span row_keys = keys_of_row(qi, off, nk, p.causal, p.window);  // the keys row qi sees
   FragAddr<T> fa;
   fa.init(lane);
   TileLoader<T, C::BN, C::THREADS> kld, vld;
@@ -139,11 +140,13 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
       for (int s = 0; s < kD / KS; ++s) st[mt] = M::mma(fa.row(Ks, mt, s), qf[s], st[mt]);
     }
     if constexpr (!FULL) {
+      // key of register r in tile mt: kbase + 4h + (32 mt + 8 (r/4) + r%4), a constant per element
+      const int k0 = kbase + 4 * h;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          st[mt][r] = visible(qi, kbase + 32 * mt + crow(r, h), off, nk, p.causal, p.window) ? st[mt][r] : -INFINITY;
+          st[mt][r] = in_span(k0 + 32 * mt + 8 * (r / 4) + r % 4, row_keys) ? st[mt][r] : -INFINITY;
     }
   };
   // P = exp2(s * sl2 + neg_m) in place, rounded into operands; returns the lane's
