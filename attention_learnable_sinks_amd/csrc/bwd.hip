@@ -537,13 +537,18 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_finish_kernel(BwdArgs a) {
   const FwdArgs& f = a.f;
-  if (blockIdx.x == 0) {
-    for (int hh = threadIdx.x; hh < f.hq; hh += blockDim.x) {
-      const float* part = a.dsink_part + (size_t)hh * a.pre_blocks;
-      float s = 0.f;
-      for (int j = 0; j < a.pre_blocks; ++j) s += part[j];
-      a.dsinks[hh] = s;
-    }
+  if ((int)blockIdx.x < f.hq) {
+    // dS_h of head blockIdx.x: the preprocess partials, summed in a fixed order
+    // (strided per thread, then a fixed butterfly and the four wavefronts in order).
+    const float* part = a.dsink_part + (size_t)blockIdx.x * a.pre_blocks;
+    float acc = 0.f;
+    for (int j = threadIdx.x; j < a.pre_blocks; j += blockDim.x) acc += part[j];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+    __shared__ float red[4];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) a.dsinks[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
   }
   if (a.splits > 1) {
     const size_t n4 = (size_t)f.total_k * f.hkv * kD / 4;
@@ -646,6 +651,7 @@ hipError_t launch_bwd_finish(const BwdArgs& a, int fp32, hipStream_t stream) {
     if (blocks > 4096) blocks = 4096;
     if (blocks == 0) blocks = 1;
   }
+  if (blocks < (size_t)a.f.hq) blocks = a.f.hq;  // one block per head for dS_h
   if (fp32)
     hipLaunchKernelGGL(bwd_finish_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   else

@@ -171,16 +171,22 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
     Frag pf[NP];
     scores(st, Ks, kbase, full_tag);
     float tsum = probs(st, pf, -m_run);  // m_run = -inf gives inf / NaN: caught below
-    if (__any(!(tsum <= kTileSumMax))) {
+    const bool over = !(tsum <= kTileSumMax);
+    if (__any(over)) {
       // Slow path (rare): raise the running max to this tile's row max.  The K
-      // tile is still in LDS, so the scores are simply computed again.
+      // tile is still in LDS, so the scores are simply computed again.  Only rows
+      // whose own tile sum broke the bound change anything, so a row's result never
+      // depends on the other rows of the wavefront (a row computed alone, e.g. one
+      // decode step, comes out bitwise the same as in a full forward).
+      const bool row_over = halves_max(over ? 1.f : 0.f) > 0.f;  // either half of the row
       scores(st, Ks, kbase, full_tag);
       float mx = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[mt][r]);
-      const float m_new = fmaxf(m_run, halves_max(mx) * sl2);
+      mx = halves_max(mx) * sl2;
+      const float m_new = row_over ? fmaxf(m_run, mx) : m_run;
       const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);  // 0 when m_run = -inf
       l_run *= alpha;
 #pragma unroll

@@ -183,6 +183,37 @@ def test_running_max_raised_mid_row(gpu_lib, dtype):
     _full_case(gpu_lib, inp, f"growing scores {dtype}", tol=2e-4 if dtype == "fp32" else None)
 
 
+@pytest.mark.parametrize("window", [0, 50])
+def test_rows_alone_match_the_full_forward_bitwise(gpu_lib, window):
+    """Inference-style calls -- one decode row against its whole prefix, or a chunk
+    of rows -- give bitwise the same O, LSE and dQ rows as the full training call.
+    Bottom-right alignment plus key tiles at absolute key positions make a row's
+    arithmetic independent of the other rows it is computed with; the key ramp makes
+    some rows raise their running max mid-sequence, which must not leak into others."""
+    n = 300
+    inp = random_case([n], 8, 2, 64, "bf16", seed=23, window=window)
+    ramp = torch.linspace(1.0, 30.0, n)
+    inp["k"] = (inp["k"].float() * ramp[:, None, None]).to(torch.bfloat16)
+    d = to_dev(inp)
+    sc = inp["softmax_scale"]
+    cu = torch.tensor([0, n], dtype=torch.int32, device="cuda")
+    o_full, lse_full = gpu_lib.fwd(d["q"], d["k"], d["v"], d["sinks"], cu, cu, n, n, sc, True, window)
+    dq_full = gpu_lib.bwd(d["q"], d["k"], d["v"], d["sinks"], o_full, lse_full, d["dout"], cu, cu, n, n, sc,
+                          True, window)[0]
+    for r0, r1 in [(299, 300), (0, 1), (131, 132), (64, 101), (200, 300)]:
+        print(f"[case] rows {r0}..{r1} window {window}", flush=True)
+        cq = torch.tensor([0, r1 - r0], dtype=torch.int32, device="cuda")
+        ck = torch.tensor([0, r1], dtype=torch.int32, device="cuda")
+        q, k, v = d["q"][r0:r1].contiguous(), d["k"][:r1].contiguous(), d["v"][:r1].contiguous()
+        o, lse = gpu_lib.fwd(q, k, v, d["sinks"], cq, ck, r1 - r0, r1, sc, True, window)
+        dq = gpu_lib.bwd(q, k, v, d["sinks"], o, lse, d["dout"][r0:r1].contiguous(), cq, ck, r1 - r0, r1, sc,
+                         True, window)[0]
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_full[r0:r1]), (r0, r1, "o")
+        assert torch.equal(lse, lse_full[:, r0:r1]), (r0, r1, "lse")
+        assert torch.equal(dq, dq_full[r0:r1]), (r0, r1, "dq")
+
+
 def test_autograd_wrapper(gpu_lib):
     inp = to_dev(random_case([150, 90], 4, 2, 64, "fp32", seed=18))
     q, k, v, s = (inp[n].clone().requires_grad_(True) for n in ("q", "k", "v", "sinks"))
