@@ -118,6 +118,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this size first (for counter calibration)")
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="extra steps, each after rewriting a 512 MiB buffer (L2 and MALL flushed), timed apart")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -171,6 +173,24 @@ def main():
     kern = als.timing_read()
     als.timing_enable(False)
 
+    # Cold-cache steps: a 512 MiB write between steps evicts L2 and the MALL; only the
+    # library's kernels are timed (HIP events around each launch).
+    cold = None
+    if args.cold_steps > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        als.timing_enable(True)
+        for _ in range(args.cold_steps):
+            flush.fill_(1)
+            step()
+        torch.cuda.synchronize()
+        kc = als.timing_read()
+        als.timing_enable(False)
+        del flush
+        per_c = {k: v[1] / v[0] for k, v in kc.items()}
+        cold = {"fwd_ms": round(per_c.get("attn_sink_fwd_kernel", float("nan")), 5),
+                "bwd_ms": round(sum(v for k, v in per_c.items() if k != "attn_sink_fwd_kernel"), 5),
+                "steps": args.cold_steps}
+
     pairs = count_pairs(w.seqlens, causal, window)
     fwd_flop = 4 * 64 * pairs * w.num_heads_q
     bwd_flop = 10 * 64 * pairs * w.num_heads_q
@@ -186,16 +206,31 @@ def main():
     dom = max(per, key=per.get)
     elem = 2 if w.dtype == "bf16" else 4
     t_tok, hq, hkv = w.total, w.num_heads_q, w.num_heads_kv
+    mfma_peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    # Algorithmic bytes per launch (each operand moved once) and FLOP per launch.
+    qb, kb = t_tok * hq * 64 * elem, t_tok * hkv * 64 * elem  # one [T, Hq, 64] / [T, Hkv, 64] tensor
+    rows = t_tok * hq * 4                                       # one fp32 value per row and head
+    kern_bytes = {
+        "attn_sink_fwd_kernel": qb + 2 * kb + qb + rows,                 # Q, K, V -> O, LSE
+        "attn_sink_bwd_pre_kernel": 2 * qb + rows + 2 * rows,            # O, dO, LSE -> lse*log2e, -D
+        "attn_sink_bwd_dq_kernel": 2 * qb + 2 * kb + 2 * rows + qb,      # Q, dO, K, V, rows -> dQ
+        "attn_sink_bwd_dkdv_kernel": 2 * qb + 2 * kb + 2 * rows + 2 * kb,  # Q, dO, K, V, rows -> dK, dV
+        "attn_sink_bwd_finish_kernel": 2 * kb,
+    }
     gemm_d = {"attn_sink_fwd_kernel": 4, "attn_sink_bwd_dq_kernel": 6, "attn_sink_bwd_dkdv_kernel": 8}
-    if dom in gemm_d:
-        work, unit, bound = gemm_d[dom] * 64 * pairs * hq / 1e12, "TFLOP/s", "mfma"
-        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    ridge = mfma_peak * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP per byte where the two peaks meet
+    flop = gemm_d.get(dom, 0) * 64 * pairs * hq
+    byts = kern_bytes.get(dom, 0)
+    if flop > 0 and flop / max(byts, 1) >= ridge:
+        work, unit, bound, peak = flop / 1e12, "TFLOP/s", "mfma", mfma_peak
     else:
-        byts = t_tok * hq * 64 * elem * 2 + t_tok * hq * 4 * 2  # read O, dO, LSE; write D
         work, unit, bound, peak = byts / 1e9, "GB/s", "hbm", PEAK_HBM_GBS
     achieved = work / (per[dom] * 1e-3)
     roofline = dict(bound=bound, achieved=round(achieved, 3), peak=peak, unit=unit, frac=round(achieved / peak, 4),
-                    traffic=read_traffic(args.workload, dom), kernel=dom, launch_ms=round(per[dom], 5))
+                    traffic=read_traffic(args.workload, dom), kernel=dom, launch_ms=round(per[dom], 5),
+                    flop_per_byte=round(flop / max(byts, 1), 1))
+    fwd_bytes = kern_bytes["attn_sink_fwd_kernel"]
+    bwd_bytes = 3 * qb + 2 * kb + rows + qb + 2 * kb + rows  # Q K V O dO LSE -> dQ dK dV, plus D (37,376 B per token at 64/8 heads)
 
     cpu, errs = None, {}
     if not args.no_cpu:
@@ -221,9 +256,14 @@ def main():
                    "causal": bool(causal), "window": int(window), "softmax_scale": scale},
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "fwd": {"ms": round(fwd_ms, 5), "tflops": round(fwd_flop / (fwd_ms * 1e-3) / 1e12, 3),
-                "frac_of_peak": round(fwd_flop / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+                "frac_of_peak": round(fwd_flop / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "algorithmic_gbs": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9, 1),
+                "frac_of_hbm": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "bwd": {"ms": round(bwd_ms, 5), "tflops": round(bwd_flop / (bwd_ms * 1e-3) / 1e12, 3),
-                "frac_of_peak": round(bwd_flop / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+                "frac_of_peak": round(bwd_flop / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "algorithmic_gbs": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9, 1),
+                "frac_of_hbm": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "cold_cache": cold,
         "kernels_ms_per_launch": {k: round(v, 5) for k, v in per.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,
