@@ -21,8 +21,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["load", "fwd", "bwd", "bwd_workspace_bytes", "Shape", "AttnSinkError", "sink_attention",
-           "timing_enable", "timing_read", "LIB_PATH"]
+__all__ = ["load", "fwd", "fwd_decode", "fwd_decode_workspace_bytes", "bwd", "bwd_workspace_bytes", "Shape",
+           "AttnSinkError", "sink_attention", "timing_enable", "timing_read", "LIB_PATH"]
 
 # ATTN_SINK_LIBRARY may point at another build of the same library (e.g. a tuning variant).
 LIB_PATH = os.environ.get("ATTN_SINK_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
@@ -73,6 +73,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     vp, sp, st = ctypes.c_void_p, ctypes.POINTER(Shape), ctypes.c_int
     lib.attn_sink_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp]
     lib.attn_sink_fwd.restype = st
+    lib.attn_sink_fwd_decode.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.attn_sink_fwd_decode.restype = st
+    lib.attn_sink_fwd_decode_workspace_bytes.argtypes = [sp]
+    lib.attn_sink_fwd_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_sink_bwd_workspace_bytes.argtypes = [sp]
     lib.attn_sink_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_sink_bwd.argtypes = [sp] + [vp] * 12 + [ctypes.c_size_t, vp]
@@ -148,6 +152,37 @@ def fwd(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k=None, max_seqlen_q=None, max_
                               _stream(q.device))
     if st != OK:
         raise AttnSinkError(st, "attn_sink_fwd")
+    return o, lse
+
+
+def fwd_decode_workspace_bytes(shape: Shape) -> int:
+    return int(_lib().attn_sink_fwd_decode_workspace_bytes(ctypes.byref(shape)))
+
+
+def fwd_decode(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None, max_seqlen_k=None,
+               softmax_scale=None, causal=True, window=0, workspace=None, out=None, lse=None):
+    """Forward for a few new rows per sequence against a long key range (decoding
+    step or short chunk against a KV cache), split over keys.  Same arguments and
+    results as fwd(); needs (Hq / Hkv) * max_seqlen_q <= 32.  `workspace` (uint8
+    device tensor of at least fwd_decode_workspace_bytes bytes) is allocated here
+    when not given."""
+    _check_tensors(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k)
+    if max_seqlen_q is None:
+        max_seqlen_q = int((cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max().item()) if cu_seqlens_q.numel() > 1 else 0
+    if max_seqlen_k is None:
+        max_seqlen_k = int((cu_seqlens_k[1:] - cu_seqlens_k[:-1]).max().item()) if cu_seqlens_k.numel() > 1 else 0
+    if softmax_scale is None:
+        softmax_scale = q.shape[2] ** -0.5
+    shape = make_shape(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale, causal, window)
+    if workspace is None:
+        workspace = torch.empty(max(fwd_decode_workspace_bytes(shape), 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty(q.shape[1], q.shape[0], dtype=torch.float32, device=q.device) if lse is None else lse
+    st = _lib().attn_sink_fwd_decode(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(o),
+                                     _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(q.device))
+    if st != OK:
+        raise AttnSinkError(st, "attn_sink_fwd_decode")
     return o, lse
 
 

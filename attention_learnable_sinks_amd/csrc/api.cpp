@@ -20,6 +20,8 @@ const char* kernel_name(int id) {
     case K_BWD_DQ: return "attn_sink_bwd_dq_kernel";
     case K_BWD_DKDV: return "attn_sink_bwd_dkdv_kernel";
     case K_BWD_FINISH: return "attn_sink_bwd_finish_kernel";
+    case K_DEC_PARTIAL: return "attn_sink_decode_partial_kernel";
+    case K_DEC_MERGE: return "attn_sink_decode_merge_kernel";
     default: return "?";
   }
 }
@@ -131,6 +133,38 @@ attn_sink_status attn_sink_fwd(const attn_sink_shape* shape, const void* q, cons
   FwdArgs a = fwd_args(shape, q, k, v, sinks, o, lse);
   const int fp32 = shape->dtype == ATTN_SINK_FP32;
   return timed_launch(K_FWD, stream, [&] { return launch_fwd(a, fp32, stream); });
+}
+
+size_t attn_sink_fwd_decode_workspace_bytes(const attn_sink_shape* shape) {
+  if (check_shape(shape) != ATTN_SINK_OK) return 0;
+  if (!decode_supported(shape->num_heads_q, shape->num_heads_kv, shape->max_seqlen_q)) return 0;
+  return decode_workspace_layout(shape->num_heads_kv, shape->num_seqs, shape->max_seqlen_q, shape->max_seqlen_k,
+                                 shape->window).total;
+}
+
+attn_sink_status attn_sink_fwd_decode(const attn_sink_shape* shape, const void* q, const void* k, const void* v,
+                                      const float* sinks, void* o, float* lse, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  attn_sink_status st = check_shape(shape);
+  if (st != ATTN_SINK_OK) return st;
+  if (!decode_supported(shape->num_heads_q, shape->num_heads_kv, shape->max_seqlen_q)) return ATTN_SINK_ERR_UNSUPPORTED;
+  const bool any_q = shape->total_q > 0, any_k = shape->total_k > 0;
+  if (!sinks || (any_q && (!q || !o || !lse)) || (any_k && (!k || !v))) return ATTN_SINK_ERR_INVALID_ARG;
+  const DecodeWorkspace ws = decode_workspace_layout(shape->num_heads_kv, shape->num_seqs, shape->max_seqlen_q,
+                                                     shape->max_seqlen_k, shape->window);
+  if (!workspace || workspace_bytes < ws.total || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return ATTN_SINK_ERR_WORKSPACE;
+  if (!any_q) return ATTN_SINK_OK;
+  DecodeArgs a;
+  a.f = fwd_args(shape, q, k, v, sinks, o, lse);
+  char* base = static_cast<char*>(workspace);
+  a.part_o = reinterpret_cast<float*>(base + ws.part_o);
+  a.part_ml = reinterpret_cast<float*>(base + ws.part_ml);
+  a.splits = ws.splits;
+  const int fp32 = shape->dtype == ATTN_SINK_FP32;
+  st = timed_launch(K_DEC_PARTIAL, stream, [&] { return launch_decode_partial(a, fp32, stream); });
+  if (st != ATTN_SINK_OK) return st;
+  return timed_launch(K_DEC_MERGE, stream, [&] { return launch_decode_merge(a, fp32, stream); });
 }
 
 size_t attn_sink_bwd_workspace_bytes(const attn_sink_shape* shape) {

@@ -38,8 +38,19 @@ struct BwdArgs {
   int splits;         // workgroups sharing one kv head's query-head group in bwd_dkdv
 };
 
+// Forward for a few query rows per sequence against long key ranges, split over keys.
+struct DecodeArgs {
+  FwdArgs f;
+  float* part_o;   // [num_seqs * hkv, splits, 32 columns, 64]: unnormalised O of each key split
+  float* part_ml;  // [num_seqs * hkv, splits, 32 columns, 2]: (running max, sum) in the exp2 domain
+  int splits;      // key splits per (sequence, kv head)
+};
+
 // Kernel identifiers for the opt-in timing records.
-enum KernelId { K_FWD = 0, K_BWD_PRE = 1, K_BWD_DQ = 2, K_BWD_DKDV = 3, K_BWD_FINISH = 4, K_COUNT = 5 };
+enum KernelId {
+  K_FWD = 0, K_BWD_PRE = 1, K_BWD_DQ = 2, K_BWD_DKDV = 3, K_BWD_FINISH = 4,
+  K_DEC_PARTIAL = 5, K_DEC_MERGE = 6, K_COUNT = 7
+};
 const char* kernel_name(int id);
 
 // Workspace layout for a backward call; offsets in bytes from the workspace base.
@@ -50,11 +61,21 @@ struct BwdWorkspace {
 BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k, int num_seqs);
 int bwd_head_splits(int hq, int hkv, int total_k, int num_seqs);
 
+struct DecodeWorkspace {
+  size_t part_o, part_ml, total;
+  int splits;
+};
+DecodeWorkspace decode_workspace_layout(int hkv, int num_seqs, int max_q, int max_k, int window);
+// The query heads of one kv head times the rows of one sequence fill at most 32 columns.
+bool decode_supported(int hq, int hkv, int max_q);
+
 // Each launcher enqueues one kernel on `stream` and returns hipGetLastError().
 hipError_t launch_fwd(const FwdArgs& a, int fp32, hipStream_t stream);
 hipError_t launch_bwd_pre(const BwdArgs& a, int fp32, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int fp32, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int fp32, hipStream_t stream);
 hipError_t launch_bwd_finish(const BwdArgs& a, int fp32, hipStream_t stream);
+hipError_t launch_decode_partial(const DecodeArgs& a, int fp32, hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeArgs& a, int fp32, hipStream_t stream);
 
 }  // namespace attn_sink

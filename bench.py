@@ -26,13 +26,16 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (vector and MFMA)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+# Sources of the training kernels (forward, backward) and of the decoding-step kernels:
+# a counter summary is valid only for the digest of the sources of its kernel.
 KERNEL_SOURCES = ["attention_learnable_sinks_amd/csrc/common.h", "attention_learnable_sinks_amd/csrc/fwd.hip",
                   "attention_learnable_sinks_amd/csrc/bwd.hip"]
+DECODE_SOURCES = ["attention_learnable_sinks_amd/csrc/common.h", "attention_learnable_sinks_amd/csrc/decode.hip"]
 
 
-def source_digest() -> str:
+def source_digest(paths=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in paths:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -49,7 +52,7 @@ def read_traffic(workload: str, kernel: str):
         if ":" in line:
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_digest") != source_digest():
+    if kv.get("source_digest") != source_digest(DECODE_SOURCES if "decode" in kernel else KERNEL_SOURCES):
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
@@ -107,6 +110,64 @@ def cpu_baseline(inp: dict, workload, pairs: int, budget_s: float = 12.0, gpu_ou
                        f"heads), forward+backward, float64 numpy, {t_total:.1f} s"), errs
 
 
+def decode_bench(als, torch, dev, steps: int, warmup: int) -> dict:
+    """Time the decoding-step forward (attn_sink_fwd_decode) on the rollout decoding
+    workload, each layer kind, with the training forward kernel on the same inputs
+    beside it.  Algorithmic bytes per call: the K and V rows every sequence's new rows
+    can see (whole cache, or the window), Q, and O + LSE written once."""
+    from workloads import DECODE_WORKLOADS, make_decode_inputs
+
+    w = DECODE_WORKLOADS["decode_rollout"]
+    res = {"workload": w.name, "source_digest": source_digest(DECODE_SOURCES),
+           "num_seqs": len(w.cache_lens), "new_rows": w.new_rows,
+           "cache_keys": int(sum(w.cache_lens)), "num_heads_q": w.num_heads_q, "num_heads_kv": w.num_heads_kv,
+           "layers": []}
+    for layer in range(len(w.layers)):
+        inp = make_decode_inputs(w, layer)
+        d = {k: inp[k].to(dev).contiguous() for k in ("q", "k", "v", "sinks", "cu_seqlens_q", "cu_seqlens_k")}
+        args = (d["q"], d["k"], d["v"], d["sinks"], d["cu_seqlens_q"], d["cu_seqlens_k"], inp["max_seqlen_q"],
+                inp["max_seqlen_k"], inp["softmax_scale"], inp["causal"], inp["window"])
+        shape = als.make_shape(d["q"], d["k"], d["cu_seqlens_q"], d["cu_seqlens_k"], inp["max_seqlen_q"],
+                               inp["max_seqlen_k"], inp["softmax_scale"], inp["causal"], inp["window"])
+        ws = torch.empty(als.fwd_decode_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+        o = torch.empty_like(d["q"])
+        lse = torch.empty(w.num_heads_q, d["q"].shape[0], dtype=torch.float32, device=dev)
+        timings = {}
+        for name, call in (("decode", lambda: als.fwd_decode(*args, workspace=ws, out=o, lse=lse)),
+                           ("fwd", lambda: als.fwd(*args, out=o, lse=lse))):
+            for _ in range(warmup):
+                call()
+            torch.cuda.synchronize()
+            als.timing_enable(True)
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                call()
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            kern = als.timing_read()
+            als.timing_enable(False)
+            timings[name] = ((t1 - t0) * 1e3 / steps, {k: v[1] / v[0] for k, v in kern.items()})
+        window, rows = inp["window"], w.new_rows
+        keys = sum(min(n, window + rows - 1) if window > 0 else n for n in w.cache_lens)
+        elem = 2 if w.dtype == "bf16" else 4
+        tq = d["q"].shape[0]
+        byts = 2 * keys * w.num_heads_kv * 64 * elem + 2 * tq * w.num_heads_q * 64 * elem + tq * w.num_heads_q * 4
+        dec_ms = sum(timings["decode"][1].values())
+        part_ms = timings["decode"][1].get("attn_sink_decode_partial_kernel", float("nan"))
+        kv_part = 2 * keys * w.num_heads_kv * 64 * elem + tq * w.num_heads_q * 64 * elem  # partial kernel: K, V, Q
+        res["layers"].append({
+            "window": int(window), "visible_keys": int(keys), "algorithmic_bytes": int(byts),
+            "us_per_call": round(timings["decode"][0] * 1e3, 2),
+            "kernels_us": {k: round(v * 1e3, 2) for k, v in timings["decode"][1].items()},
+            "gbs": round(byts / (dec_ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm": round(byts / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "partial_kernel_frac_of_hbm": round(kv_part / (part_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "fwd_kernel_us": round(sum(timings["fwd"][1].values()) * 1e3, 2),
+        })
+        del ws, o, lse, d
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,6 +179,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this size first (for counter calibration)")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decoding-step leg")
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="extra steps, each after rewriting a 512 MiB buffer (L2 and MALL flushed), timed apart")
     args = ap.parse_args()
@@ -232,6 +294,8 @@ def main():
     fwd_bytes = kern_bytes["attn_sink_fwd_kernel"]
     bwd_bytes = 3 * qb + 2 * kb + rows + qb + 2 * kb + rows  # Q K V O dO LSE -> dQ dK dV, plus D (37,376 B per token at 64/8 heads)
 
+    dec = None if args.no_decode else decode_bench(als, torch, dev, max(args.steps, 10), max(args.warmup, 2))
+
     cpu, errs = None, {}
     if not args.no_cpu:
         host = {k: t.float().cpu().numpy().astype(np.float64) for k, t in
@@ -264,6 +328,7 @@ def main():
                 "algorithmic_gbs": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9, 1),
                 "frac_of_hbm": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "cold_cache": cold,
+        "decode": dec,
         "kernels_ms_per_launch": {k: round(v, 5) for k, v in per.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,

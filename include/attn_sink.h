@@ -63,8 +63,8 @@ extern "C" {
 typedef enum {
   ATTN_SINK_OK = 0,
   ATTN_SINK_ERR_INVALID_ARG = 1,  /* null pointer, bad count, Hq % Hkv != 0, ... */
-  ATTN_SINK_ERR_UNSUPPORTED = 2,  /* well-formed but not built: head_dim != 64, dtype */
-  ATTN_SINK_ERR_WORKSPACE = 3,    /* backward workspace missing or smaller than required */
+  ATTN_SINK_ERR_UNSUPPORTED = 2,  /* well-formed but not built: head_dim != 64, dtype, decode width */
+  ATTN_SINK_ERR_WORKSPACE = 3,    /* workspace missing, misaligned or smaller than required */
   ATTN_SINK_ERR_HIP = 4           /* the HIP runtime refused a launch */
 } attn_sink_status;
 
@@ -100,6 +100,34 @@ attn_sink_status attn_sink_fwd(const attn_sink_shape* shape,
                                void* o, float* lse,
                                hipStream_t stream);
 
+/* Forward for a few new query rows per sequence against long key ranges: a
+ * decoding step, or a short chunk, against a KV cache.  Same function, inputs,
+ * layouts, masks and outputs as attn_sink_fwd (sub-sections 带汇聚的注意力 and
+ * 数学公式 of the page cited above), organised for this shape: the key range of
+ * every (sequence, kv head) is split over many workgroups that each keep an
+ * online softmax without the sink, and a merge kernel combines the splits in a
+ * fixed order and adds exp(S_h) to the normaliser exactly once.  The results equal
+ * attn_sink_fwd's up to floating-point rounding order (not bitwise) and are
+ * bitwise reproducible from run to run.
+ * Requires (Hq / Hkv) * max_seqlen_q <= 32 (the query heads of one kv head times
+ * the new rows of one sequence share one 32-column matrix-core block), else
+ * ATTN_SINK_ERR_UNSUPPORTED; rows are bottom-right aligned with the keys, as in
+ * attn_sink_fwd (row i of n_q sits at key position i + n_k - n_q).
+ * workspace: device memory of at least attn_sink_fwd_decode_workspace_bytes(shape)
+ * bytes, 256-byte aligned, owned by the caller, contents need not be initialised
+ * and are garbage afterwards; ATTN_SINK_ERR_WORKSPACE if missing, misaligned or
+ * too small. */
+attn_sink_status attn_sink_fwd_decode(const attn_sink_shape* shape,
+                                      const void* q, const void* k, const void* v,
+                                      const float* sinks,
+                                      void* o, float* lse,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+
+/* Bytes of device workspace attn_sink_fwd_decode needs for `shape` (0 on an
+ * invalid or unsupported shape). */
+size_t attn_sink_fwd_decode_workspace_bytes(const attn_sink_shape* shape);
+
 /* Bytes of device workspace attn_sink_bwd needs for `shape` (0 on invalid shape). */
 size_t attn_sink_bwd_workspace_bytes(const attn_sink_shape* shape);
 
@@ -127,7 +155,7 @@ attn_sink_status attn_sink_bwd(const attn_sink_shape* shape,
 const char* attn_sink_status_string(attn_sink_status status);
 
 /* Opt-in per-kernel timing for measurement harnesses.  While enabled, every
- * kernel the two entry points launch is bracketed by HIP events on the launch
+ * kernel the compute entry points launch is bracketed by HIP events on the launch
  * stream (this adds event records to the stream, nothing else).
  * attn_sink_timing_enable(1) clears earlier records; (0) stops recording.
  * attn_sink_timing_read synchronises on the recorded events and fills, for up to

@@ -28,6 +28,7 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["attn_sink_fwd", "attn_sink_bwd", "attn_sink_bwd_workspace_bytes",
+                                  "attn_sink_fwd_decode", "attn_sink_fwd_decode_workspace_bytes",
                                   "attn_sink_status_string", "attn_sink_timing_enable", "attn_sink_timing_read"])
 
 
@@ -88,9 +89,71 @@ def test_bwd_rejects_bad_shape(lib, kw, status):
     assert lib.attn_sink_bwd_workspace_bytes(ctypes.byref(s)) == 0
 
 
+def _decode_shape(**kw):
+    base = dict(num_heads_q=64, num_heads_kv=8, num_seqs=4, total_q=4, total_k=4 * 8192, max_seqlen_q=1,
+                max_seqlen_k=8192)
+    base.update(kw)
+    return _shape(**base)
+
+
+@pytest.mark.parametrize("kw,status", BAD_SHAPES, ids=[str(k) for k, _ in BAD_SHAPES])
+def test_fwd_decode_rejects_bad_shape(lib, kw, status):
+    s = _shape(**kw)
+    assert lib.attn_sink_fwd_decode(ctypes.byref(s), *[FAKE] * 7, 1 << 40, None) == status
+    assert lib.attn_sink_fwd_decode_workspace_bytes(ctypes.byref(s)) == 0
+
+
+@pytest.mark.parametrize("hq,hkv,max_q,ok", [(64, 8, 4, True), (64, 8, 5, False), (8, 8, 32, True),
+                                              (8, 8, 33, False), (64, 1, 1, False), (32, 1, 1, True),
+                                              (24, 8, 10, True), (24, 8, 11, False)])
+def test_fwd_decode_width_limit(lib, hq, hkv, max_q, ok):
+    """(Hq / Hkv) * max_seqlen_q <= 32: the query heads of a kv head times the new
+    rows share one 32-column block."""
+    s = _decode_shape(num_heads_q=hq, num_heads_kv=hkv, max_seqlen_q=max_q, total_q=4 * max_q)
+    n = lib.attn_sink_fwd_decode_workspace_bytes(ctypes.byref(s))
+    st = lib.attn_sink_fwd_decode(ctypes.byref(s), *[FAKE] * 7, 0, None)
+    if ok:
+        assert n > 0 and st == als.ERR_WORKSPACE  # passes the width check, stops at the workspace
+    else:
+        assert n == 0 and st == als.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("slot", range(6))
+def test_fwd_decode_rejects_null_tensor(lib, slot):
+    ptrs = [FAKE] * 6
+    ptrs[slot] = None
+    s = _decode_shape()
+    assert lib.attn_sink_fwd_decode(ctypes.byref(s), *ptrs, FAKE, 1 << 40, None) == als.ERR_INVALID_ARG
+
+
+def test_fwd_decode_workspace(lib):
+    """Partials: per (sequence, kv head, key split) 32 columns of 64 values plus a
+    (max, sum) pair, in float32; the split count targets about 1024 workgroups
+    with at least one 64-key tile per wavefront (four per workgroup)."""
+    s = _decode_shape()  # 4 sequences x 8 kv heads = 32 groups; 8192 keys = 128 tiles
+    n = lib.attn_sink_fwd_decode_workspace_bytes(ctypes.byref(s))
+    splits = 32  # ceil(1024 / 32) = 32 <= ceil(128 / 4)
+    expect = 32 * splits * 32 * (64 + 2) * 4
+    assert expect <= n <= expect + 2 * 256
+    s = _decode_shape(window=128)  # 128 + 1 - 1 keys: 2 tiles + 1 straddled -> one split
+    n = lib.attn_sink_fwd_decode_workspace_bytes(ctypes.byref(s))
+    assert 32 * 1 * 32 * 66 * 4 <= n <= 32 * 1 * 32 * 66 * 4 + 512
+    s = _decode_shape(num_seqs=1, total_q=1, total_k=131072, max_seqlen_k=131072)  # 8 groups
+    n = lib.attn_sink_fwd_decode_workspace_bytes(ctypes.byref(s))
+    expect = 8 * 128 * 32 * 66 * 4
+    assert expect <= n <= expect + 512
+    args = [FAKE] * 7
+    need = lib.attn_sink_fwd_decode_workspace_bytes(ctypes.byref(_decode_shape()))
+    s = _decode_shape()
+    assert lib.attn_sink_fwd_decode(ctypes.byref(s), *args[:6], FAKE, need - 1, None) == als.ERR_WORKSPACE
+    assert lib.attn_sink_fwd_decode(ctypes.byref(s), *args[:6], None, need, None) == als.ERR_WORKSPACE
+    assert lib.attn_sink_fwd_decode(ctypes.byref(s), *args[:6], FAKE + 8, need, None) == als.ERR_WORKSPACE
+
+
 def test_null_shape(lib):
     assert lib.attn_sink_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == als.ERR_INVALID_ARG
     assert lib.attn_sink_bwd_workspace_bytes(None) == 0
+    assert lib.attn_sink_fwd_decode_workspace_bytes(None) == 0
 
 
 @pytest.mark.parametrize("slot", range(6))

@@ -102,3 +102,62 @@ def random_case(seqlens, hq, hkv, d=64, dtype="bf16", seed=0, causal=True, windo
     w = Workload("case", tuple(seqlens), hq, hkv, d, dtype, seed, ((causal, window, sink_dist),),
                  softmax_scale=(1.0 / np.sqrt(d)) if scale is None else scale)
     return make_inputs(w)
+
+
+# ----------------------------------------------------------------------------- decoding steps
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """One decoding step of a rollout batch: each sequence brings `new_rows` query
+    rows and attends to its whole KV cache (the cache includes the new rows' keys,
+    which sit at its end)."""
+    name: str
+    cache_lens: tuple         # keys per sequence
+    new_rows: int             # query rows per sequence
+    num_heads_q: int
+    num_heads_kv: int
+    head_dim: int
+    dtype: str
+    seed: int
+    layers: tuple             # ((causal, window, sink_dist), ...)
+    softmax_scale: float = 0.125
+
+
+# A rollout batch mid-generation: 64 sequences whose caches hold prompt + response
+# so far (uniform in [1024, 16384], the same range as the packed training batch),
+# one new token each; GPT-OSS alternates full and 128-key sliding-window layers.
+DECODE_WORKLOADS = {
+    "decode_rollout": DecodeWorkload("decode_rollout", varlen_lengths(5, n=64), 1, 64, 8, 64, "bf16", 6,
+                                     ((True, 0, ("normal",)), (True, 128, ("normal",)))),
+}
+
+
+def make_decode_inputs(w: DecodeWorkload, layer: int = 0, seed: Optional[int] = None,
+                       new_rows=None) -> dict:
+    """Host tensors for one layer call of a decoding step.  Draw order: q, k, v,
+    then one sink vector per layer (float32 from one torch.Generator('cpu')).
+    `new_rows` (one count per sequence) overrides w.new_rows."""
+    gen = torch.Generator("cpu").manual_seed(w.seed if seed is None else seed)
+    nb = len(w.cache_lens)
+    rows = [w.new_rows] * nb if new_rows is None else list(new_rows)
+    tq, tk, hq, hkv, d = int(sum(rows)), int(sum(w.cache_lens)), w.num_heads_q, w.num_heads_kv, w.head_dim
+    q = torch.randn(tq, hq, d, generator=gen, dtype=torch.float32)
+    k = torch.randn(tk, hkv, d, generator=gen, dtype=torch.float32)
+    v = torch.randn(tk, hkv, d, generator=gen, dtype=torch.float32)
+    sinks = [_draw_sinks(gen, hq, lay[2]) for lay in w.layers]
+    store = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    causal, window, _ = w.layers[layer]
+    return dict(q=q.to(store), k=k.to(store), v=v.to(store), sinks=sinks[layer].contiguous(),
+                cu_seqlens_q=torch.tensor([0] + np.cumsum(rows).astype(int).tolist(), dtype=torch.int32),
+                cu_seqlens_k=torch.tensor([0] + np.cumsum(w.cache_lens).astype(int).tolist(), dtype=torch.int32),
+                causal=causal, window=window, softmax_scale=w.softmax_scale,
+                max_seqlen_q=int(max(rows)) if rows else 0,
+                max_seqlen_k=int(max(w.cache_lens)) if nb else 0)
+
+
+def decode_case(cache_lens, new_rows, hq, hkv, d=64, dtype="bf16", seed=0, causal=True, window=0,
+                sink_dist=("normal",), scale=0.125) -> dict:
+    """Small ad-hoc decoding step (tests); `new_rows` is an int or one count per sequence."""
+    rows = [new_rows] * len(cache_lens) if isinstance(new_rows, int) else list(new_rows)
+    w = DecodeWorkload("case", tuple(cache_lens), max(rows) if rows else 0, hq, hkv, d, dtype, seed,
+                       ((causal, window, sink_dist),), softmax_scale=scale)
+    return make_decode_inputs(w, new_rows=rows)
