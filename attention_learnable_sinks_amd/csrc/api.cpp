@@ -116,6 +116,11 @@ FwdArgs fwd_args(const attn_sink_shape* s, const void* q, const void* k, const v
   return a;
 }
 
+DecodeWorkspace decode_layout(const attn_sink_shape* s) {
+  return decode_workspace_layout(s->dtype == ATTN_SINK_FP32, s->num_heads_q, s->num_heads_kv, s->num_seqs,
+                                 s->max_seqlen_q, s->max_seqlen_k, s->window > 0 ? s->window : 0);
+}
+
 }  // namespace
 }  // namespace attn_sink
 
@@ -138,8 +143,7 @@ attn_sink_status attn_sink_fwd(const attn_sink_shape* shape, const void* q, cons
 size_t attn_sink_fwd_decode_workspace_bytes(const attn_sink_shape* shape) {
   if (check_shape(shape) != ATTN_SINK_OK) return 0;
   if (!decode_supported(shape->num_heads_q, shape->num_heads_kv, shape->max_seqlen_q)) return 0;
-  return decode_workspace_layout(shape->num_heads_kv, shape->num_seqs, shape->max_seqlen_q, shape->max_seqlen_k,
-                                 shape->window).total;
+  return decode_layout(shape).total;
 }
 
 attn_sink_status attn_sink_fwd_decode(const attn_sink_shape* shape, const void* q, const void* k, const void* v,
@@ -150,8 +154,7 @@ attn_sink_status attn_sink_fwd_decode(const attn_sink_shape* shape, const void* 
   if (!decode_supported(shape->num_heads_q, shape->num_heads_kv, shape->max_seqlen_q)) return ATTN_SINK_ERR_UNSUPPORTED;
   const bool any_q = shape->total_q > 0, any_k = shape->total_k > 0;
   if (!sinks || (any_q && (!q || !o || !lse)) || (any_k && (!k || !v))) return ATTN_SINK_ERR_INVALID_ARG;
-  const DecodeWorkspace ws = decode_workspace_layout(shape->num_heads_kv, shape->num_seqs, shape->max_seqlen_q,
-                                                     shape->max_seqlen_k, shape->window);
+  const DecodeWorkspace ws = decode_layout(shape);
   if (!workspace || workspace_bytes < ws.total || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
     return ATTN_SINK_ERR_WORKSPACE;
   if (!any_q) return ATTN_SINK_OK;
@@ -160,10 +163,13 @@ attn_sink_status attn_sink_fwd_decode(const attn_sink_shape* shape, const void* 
   char* base = static_cast<char*>(workspace);
   a.part_o = reinterpret_cast<float*>(base + ws.part_o);
   a.part_ml = reinterpret_cast<float*>(base + ws.part_ml);
-  a.splits = ws.splits;
+  a.chunk = ws.chunk;
+  a.max_chunks = ws.max_chunks;
+  a.cols = ws.cols;
+  a.hw = ws.hw;
   const int fp32 = shape->dtype == ATTN_SINK_FP32;
   st = timed_launch(K_DEC_PARTIAL, stream, [&] { return launch_decode_partial(a, fp32, stream); });
-  if (st != ATTN_SINK_OK) return st;
+  if (st != ATTN_SINK_OK || ws.max_chunks <= 1) return st;  // one chunk: finished in place
   return timed_launch(K_DEC_MERGE, stream, [&] { return launch_decode_merge(a, fp32, stream); });
 }
 

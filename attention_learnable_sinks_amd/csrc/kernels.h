@@ -41,9 +41,12 @@ struct BwdArgs {
 // Forward for a few query rows per sequence against long key ranges, split over keys.
 struct DecodeArgs {
   FwdArgs f;
-  float* part_o;   // [num_seqs * hkv, splits, 32 columns, 64]: unnormalised O of each key split
-  float* part_ml;  // [num_seqs * hkv, splits, 32 columns, 2]: (running max, sum) in the exp2 domain
-  int splits;      // key splits per (sequence, kv head)
+  float* part_o;   // [num_seqs * hkv, max_chunks, cols, 64]: unnormalised O of each key chunk
+  float* part_ml;  // [num_seqs * hkv, max_chunks, cols, 2]: (running max, sum) in the exp2 domain
+  int chunk;       // key tiles (of 64) per chunk
+  int max_chunks;  // chunks of the longest visible key range (grid y)
+  int cols;        // (Hq / Hkv) * max_seqlen_q: columns per (sequence, kv head)
+  int hw;          // kv heads (wavefronts) per workgroup
 };
 
 // Kernel identifiers for the opt-in timing records.
@@ -63,9 +66,9 @@ int bwd_head_splits(int hq, int hkv, int total_k, int num_seqs);
 
 struct DecodeWorkspace {
   size_t part_o, part_ml, total;
-  int splits;
+  int chunk, max_chunks, cols, hw;
 };
-DecodeWorkspace decode_workspace_layout(int hkv, int num_seqs, int max_q, int max_k, int window);
+DecodeWorkspace decode_workspace_layout(int fp32, int hq, int hkv, int num_seqs, int max_q, int max_k, int window);
 // The query heads of one kv head times the rows of one sequence fill at most 32 columns.
 bool decode_supported(int hq, int hkv, int max_q);
 

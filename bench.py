@@ -155,6 +155,12 @@ def decode_bench(als, torch, dev, steps: int, warmup: int) -> dict:
         dec_ms = sum(timings["decode"][1].values())
         part_ms = timings["decode"][1].get("attn_sink_decode_partial_kernel", float("nan"))
         kv_part = 2 * keys * w.num_heads_kv * 64 * elem + tq * w.num_heads_q * 64 * elem  # partial kernel: K, V, Q
+        part_gbs = kv_part / (part_ms * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(part_gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(part_gbs / PEAK_HBM_GBS, 4),
+                    traffic=read_traffic(w.name, "attn_sink_decode_partial_kernel") if window == 0 else None,
+                    kernel="attn_sink_decode_partial_kernel", launch_ms=round(part_ms, 5),
+                    algorithmic_bytes=int(kv_part))
         res["layers"].append({
             "window": int(window), "visible_keys": int(keys), "algorithmic_bytes": int(byts),
             "us_per_call": round(timings["decode"][0] * 1e3, 2),
@@ -163,6 +169,7 @@ def decode_bench(als, torch, dev, steps: int, warmup: int) -> dict:
             "frac_of_hbm": round(byts / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "partial_kernel_frac_of_hbm": round(kv_part / (part_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "fwd_kernel_us": round(sum(timings["fwd"][1].values()) * 1e3, 2),
+            "roofline": roof,
         })
         del ws, o, lse, d
     return res

@@ -127,21 +127,28 @@ def test_fwd_decode_rejects_null_tensor(lib, slot):
 
 
 def test_fwd_decode_workspace(lib):
-    """Partials: per (sequence, kv head, key split) 32 columns of 64 values plus a
-    (max, sum) pair, in float32; the split count targets about 1024 workgroups
-    with at least one 64-key tile per wavefront (four per workgroup)."""
-    s = _decode_shape()  # 4 sequences x 8 kv heads = 32 groups; 8192 keys = 128 tiles
-    n = lib.attn_sink_fwd_decode_workspace_bytes(ctypes.byref(s))
-    splits = 32  # ceil(1024 / 32) = 32 <= ceil(128 / 4)
-    expect = 32 * splits * 32 * (64 + 2) * 4
-    assert expect <= n <= expect + 2 * 256
-    s = _decode_shape(window=128)  # 128 + 1 - 1 keys: 2 tiles + 1 straddled -> one split
-    n = lib.attn_sink_fwd_decode_workspace_bytes(ctypes.byref(s))
-    assert 32 * 1 * 32 * 66 * 4 <= n <= 32 * 1 * 32 * 66 * 4 + 512
-    s = _decode_shape(num_seqs=1, total_q=1, total_k=131072, max_seqlen_k=131072)  # 8 groups
-    n = lib.attn_sink_fwd_decode_workspace_bytes(ctypes.byref(s))
-    expect = 8 * 128 * 32 * 66 * 4
-    assert expect <= n <= expect + 512
+    """Partials: per (sequence, kv head, key chunk) one 64-value row plus a (max,
+    sum) pair per (query head, new row) column, in float32.  Chunks are a fixed 1024
+    keys (batch invariance); with a single chunk nothing is kept (256 bytes are still
+    reported)."""
+    def parts(seqs, hkv, chunks, cols):
+        n = seqs * hkv * chunks * cols
+        return -(-n * 64 * 4 // 256) * 256 + -(-n * 2 * 4 // 256) * 256
+
+    s = _decode_shape()  # 4 sequences, 8192 keys = 8 chunks
+    assert lib.attn_sink_fwd_decode_workspace_bytes(ctypes.byref(s)) == parts(4, 8, 8, 8)
+    s = _decode_shape(max_seqlen_q=4, total_q=16)  # 8 heads x 4 rows = 32 columns
+    assert lib.attn_sink_fwd_decode_workspace_bytes(ctypes.byref(s)) == parts(4, 8, 8, 32)
+    s = _decode_shape(num_seqs=64, total_q=64, total_k=64 * 16384, max_seqlen_k=16384)
+    assert lib.attn_sink_fwd_decode_workspace_bytes(ctypes.byref(s)) == parts(64, 8, 16, 8)
+    s = _decode_shape(max_seqlen_k=1025, total_k=4 * 1025)  # 1025 keys straddle two chunks
+    assert lib.attn_sink_fwd_decode_workspace_bytes(ctypes.byref(s)) == parts(4, 8, 2, 8)
+    s = _decode_shape(max_seqlen_k=1024, total_k=4 * 1024)  # exactly one chunk: no partials
+    assert lib.attn_sink_fwd_decode_workspace_bytes(ctypes.byref(s)) == 256
+    s = _decode_shape(window=128)  # 128 keys straddle at most 5 tiles: one chunk, no partials
+    assert lib.attn_sink_fwd_decode_workspace_bytes(ctypes.byref(s)) == 256
+    s = _decode_shape(num_seqs=1, total_q=1, total_k=131072, max_seqlen_k=131072)
+    assert lib.attn_sink_fwd_decode_workspace_bytes(ctypes.byref(s)) == parts(1, 8, 128, 8)
     args = [FAKE] * 7
     need = lib.attn_sink_fwd_decode_workspace_bytes(ctypes.byref(_decode_shape()))
     s = _decode_shape()

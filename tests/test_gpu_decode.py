@@ -5,8 +5,10 @@ The cases cover what the split-K organisation can get wrong: caches shorter than
 one 64-key tile, ragged last tiles, enough keys for many splits (so the merge
 combines partials of different maxima and empty splits), new rows that see no key
 at all, sequences without new rows, every column count from 1 to 32 of the
-(query head x new row) block (G = 1, 3, 8, 32), windows that cut a tile,
-non-causal rows, and sinks at -inf and far above every score.
+(query head x new row) block (G = 1, 3, 8, 32), kv head counts that split into
+workgroups of 1, 2, 4, 6 or 8 heads, sequences finished in one chunk beside
+sequences merged from many, windows that cut a tile, non-causal rows, and sinks at
+-inf and far above every score.
 """
 
 import numpy as np
@@ -74,6 +76,8 @@ CASES = [
     ([600, 1500], 3, 16, 2, False, 100),
     ([0, 50, 10], [2, 2, 0], 8, 2, True, 0),
     ([20000], 2, 64, 8, True, 0),
+    ([300, 5000, 2], 2, 24, 12, True, 0),
+    ([4000, 90], 5, 6, 2, True, 300),
 ]
 
 
@@ -102,6 +106,27 @@ def test_decode_is_repeatable(gpu_lib):
     a = _decode(gpu_lib, inp)
     b = _decode(gpu_lib, inp)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_decode_is_batch_invariant(gpu_lib):
+    """A sequence's outputs are bitwise the same whether it is decoded alone, first or
+    last in a batch, or beside caches of other lengths (the key chunking depends on
+    the sequence alone), for full and windowed layers."""
+    for window in (0, 128):
+        big = decode_case([5000, 70, 12000, 2100], [1, 3, 2, 4], 64, 8, 64, "bf16", seed=27, window=window)
+        o_all, lse_all = _decode(gpu_lib, big)
+        cq, ck = big["cu_seqlens_q"].tolist(), big["cu_seqlens_k"].tolist()
+        for b in (0, 2, 3):
+            one = dict(big)
+            one["q"] = big["q"][cq[b]:cq[b + 1]].contiguous()
+            one["k"] = big["k"][ck[b]:ck[b + 1]].contiguous()
+            one["v"] = big["v"][ck[b]:ck[b + 1]].contiguous()
+            one["cu_seqlens_q"] = torch.tensor([0, cq[b + 1] - cq[b]], dtype=torch.int32)
+            one["cu_seqlens_k"] = torch.tensor([0, ck[b + 1] - ck[b]], dtype=torch.int32)
+            one["max_seqlen_q"], one["max_seqlen_k"] = cq[b + 1] - cq[b], ck[b + 1] - ck[b]
+            o1, lse1 = _decode(gpu_lib, one)
+            assert torch.equal(o1, o_all[cq[b]:cq[b + 1]]), (window, b)
+            assert torch.equal(lse1, lse_all[:, cq[b]:cq[b + 1]]), (window, b)
 
 
 def test_decode_minus_inf_sink(gpu_lib):
