@@ -21,8 +21,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["load", "fwd", "fwd_decode", "fwd_decode_workspace_bytes", "bwd", "bwd_workspace_bytes", "Shape",
-           "AttnSinkError", "sink_attention", "timing_enable", "timing_read", "LIB_PATH"]
+__all__ = ["load", "fwd", "fwd_decode", "fwd_decode_workspace_bytes", "merge", "bwd", "bwd_workspace_bytes",
+           "Shape", "AttnSinkError", "sink_attention", "timing_enable", "timing_read", "LIB_PATH"]
 
 # ATTN_SINK_LIBRARY may point at another build of the same library (e.g. a tuning variant).
 LIB_PATH = os.environ.get("ATTN_SINK_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
@@ -77,6 +77,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_sink_fwd_decode.restype = st
     lib.attn_sink_fwd_decode_workspace_bytes.argtypes = [sp]
     lib.attn_sink_fwd_decode_workspace_bytes.restype = ctypes.c_size_t
+    ci = ctypes.c_int
+    lib.attn_sink_merge.argtypes = [ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp]
+    lib.attn_sink_merge.restype = st
     lib.attn_sink_bwd_workspace_bytes.argtypes = [sp]
     lib.attn_sink_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_sink_bwd.argtypes = [sp] + [vp] * 12 + [ctypes.c_size_t, vp]
@@ -183,6 +186,33 @@ def fwd_decode(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None, ma
                                      _stream(q.device))
     if st != OK:
         raise AttnSinkError(st, "attn_sink_fwd_decode")
+    return o, lse
+
+
+def merge(o_parts, lse_parts, sinks, out=None, lse=None):
+    """Merge per-shard attention partials (each from fwd() with sinks = -inf over one
+    key shard) into sink attention, the sink counted once.  o_parts [P, Tq, Hq, 64]
+    (bf16 or fp32), lse_parts [P, Hq, Tq] fp32, sinks [Hq] fp32, all contiguous on the
+    device.  Returns (o [Tq, Hq, 64], lse [Hq, Tq])."""
+    if o_parts.dim() != 4 or not o_parts.is_contiguous() or not o_parts.is_cuda:
+        raise ValueError("o_parts must be a contiguous 4-d device tensor [P, Tq, Hq, d]")
+    p, tq, hq, d = o_parts.shape
+    if lse_parts.shape != (p, hq, tq) or lse_parts.dtype != torch.float32 or not lse_parts.is_contiguous():
+        raise ValueError("lse_parts must be a contiguous float32 tensor [P, Hq, Tq]")
+    if sinks.dtype != torch.float32 or sinks.numel() != hq or not sinks.is_contiguous():
+        raise ValueError("sinks must be a contiguous float32 tensor [Hq]")
+    if o_parts.dtype == torch.bfloat16:
+        dt = BF16
+    elif o_parts.dtype == torch.float32:
+        dt = FP32
+    else:
+        raise TypeError(f"unsupported dtype {o_parts.dtype}")
+    o = torch.empty(tq, hq, d, dtype=o_parts.dtype, device=o_parts.device) if out is None else out
+    lse = torch.empty(hq, tq, dtype=torch.float32, device=o_parts.device) if lse is None else lse
+    st = _lib().attn_sink_merge(dt, d, hq, tq, p, _ptr(o_parts), _ptr(lse_parts), _ptr(sinks), _ptr(o), _ptr(lse),
+                                _stream(o_parts.device))
+    if st != OK:
+        raise AttnSinkError(st, "attn_sink_merge")
     return o, lse
 
 

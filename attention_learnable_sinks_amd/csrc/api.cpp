@@ -22,6 +22,7 @@ const char* kernel_name(int id) {
     case K_BWD_FINISH: return "attn_sink_bwd_finish_kernel";
     case K_DEC_PARTIAL: return "attn_sink_decode_partial_kernel";
     case K_DEC_MERGE: return "attn_sink_decode_merge_kernel";
+    case K_MERGE: return "attn_sink_merge_kernel";
     default: return "?";
   }
 }
@@ -219,6 +220,28 @@ attn_sink_status attn_sink_bwd(const attn_sink_shape* shape, const void* q, cons
     if (st != ATTN_SINK_OK) return st;
   }
   return timed_launch(K_BWD_FINISH, stream, [&] { return launch_bwd_finish(a, fp32, stream); });
+}
+
+attn_sink_status attn_sink_merge(int dtype, int head_dim, int num_heads_q, int total_q, int num_parts,
+                                 const void* o_parts, const float* lse_parts, const float* sinks, void* o,
+                                 float* lse, hipStream_t stream) {
+  if (dtype != ATTN_SINK_BF16 && dtype != ATTN_SINK_FP32) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (head_dim != kHeadDimBuilt) return head_dim > 0 ? ATTN_SINK_ERR_UNSUPPORTED : ATTN_SINK_ERR_INVALID_ARG;
+  if (num_heads_q < 1 || total_q < 0 || num_parts < 1) return ATTN_SINK_ERR_INVALID_ARG;
+  if (!sinks) return ATTN_SINK_ERR_INVALID_ARG;
+  if (total_q > 0 && (!o_parts || !lse_parts || !o || !lse)) return ATTN_SINK_ERR_INVALID_ARG;
+  if (total_q == 0) return ATTN_SINK_OK;
+  MergeArgs a;
+  a.o_parts = o_parts;
+  a.lse_parts = lse_parts;
+  a.sinks = sinks;
+  a.o = o;
+  a.lse = lse;
+  a.parts = num_parts;
+  a.hq = num_heads_q;
+  a.total_q = total_q;
+  const int fp32 = dtype == ATTN_SINK_FP32;
+  return timed_launch(K_MERGE, stream, [&] { return launch_merge(a, fp32, stream); });
 }
 
 const char* attn_sink_status_string(attn_sink_status status) {

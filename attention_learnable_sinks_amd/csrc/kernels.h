@@ -49,10 +49,20 @@ struct DecodeArgs {
   int hw;          // kv heads (wavefronts) per workgroup
 };
 
+// Merge of per-shard attention partials (no sink) into the sink attention output.
+struct MergeArgs {
+  const void* o_parts;     // [parts, total_q, hq, 64], element type of the call
+  const float* lse_parts;  // [parts, hq, total_q], natural log, no sink
+  const float* sinks;      // [hq]
+  void* o;                 // [total_q, hq, 64]
+  float* lse;              // [hq, total_q], sink included
+  int parts, hq, total_q;
+};
+
 // Kernel identifiers for the opt-in timing records.
 enum KernelId {
   K_FWD = 0, K_BWD_PRE = 1, K_BWD_DQ = 2, K_BWD_DKDV = 3, K_BWD_FINISH = 4,
-  K_DEC_PARTIAL = 5, K_DEC_MERGE = 6, K_COUNT = 7
+  K_DEC_PARTIAL = 5, K_DEC_MERGE = 6, K_MERGE = 7, K_COUNT = 8
 };
 const char* kernel_name(int id);
 
@@ -80,5 +90,6 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int fp32, hipStream_t stream);
 hipError_t launch_bwd_finish(const BwdArgs& a, int fp32, hipStream_t stream);
 hipError_t launch_decode_partial(const DecodeArgs& a, int fp32, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, int fp32, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, int fp32, hipStream_t stream);
 
 }  // namespace attn_sink

@@ -151,6 +151,35 @@ attn_sink_status attn_sink_bwd(const attn_sink_shape* shape,
                                void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/* Merge of attention partials over disjoint key shards into sink attention, the
+ * sink counted exactly once.  This is the combine step of sequence (context)
+ * parallelism, where each device attends its query rows to one shard of the keys at
+ * a time (sequence parallelism for long rollouts: keryc.com "GPT-OSS enables agentic
+ * RL training", section Solutions; the normaliser with one exp(S_h): "Unlocking
+ * Agentic RL Training for GPT-OSS", 数学公式).
+ * Part s is what attn_sink_fwd returns for the same query rows against shard s's
+ * keys with every sink set to -INFINITY: o_parts[s] the standard-attention output
+ * over the shard, lse_parts[s] its natural-log normaliser (-inf where a row sees no
+ * key of the shard).  Writes, with the sinks given here,
+ *   M = max(S_h, max_s lse_s),  L = exp(S_h - M) + sum_s exp(lse_s - M),
+ *   o = sum_s exp(lse_s - M) o_s / L,  lse = M + log L,
+ * which equal attn_sink_fwd over all the keys up to rounding.  Parts are folded in
+ * index order (bitwise repeatable).
+ * Layouts: o_parts [num_parts, total_q, Hq, head_dim] (dtype), lse_parts
+ * [num_parts, Hq, total_q] float32, sinks [Hq] float32, o [total_q, Hq, head_dim]
+ * (dtype), lse [Hq, total_q] float32.  Outputs must not alias the inputs.
+ * The backward of the sharded attention needs no merge kernel: calling
+ * attn_sink_bwd per shard with the merged o and lse gives that shard's dk, dv and
+ * its share of dq (summed over the shards); dsinks depends only on the merged o,
+ * lse and dout, so every shard's call returns the same dsinks (take one).
+ * Errors: ATTN_SINK_ERR_UNSUPPORTED for dtype / head_dim; ATTN_SINK_ERR_INVALID_ARG
+ * for num_heads_q < 1, total_q < 0, num_parts < 1 or a null pointer. */
+attn_sink_status attn_sink_merge(int dtype, int head_dim, int num_heads_q, int total_q, int num_parts,
+                                 const void* o_parts, const float* lse_parts,
+                                 const float* sinks,
+                                 void* o, float* lse,
+                                 hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* attn_sink_status_string(attn_sink_status status);
 

@@ -28,7 +28,7 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["attn_sink_fwd", "attn_sink_bwd", "attn_sink_bwd_workspace_bytes",
-                                  "attn_sink_fwd_decode", "attn_sink_fwd_decode_workspace_bytes",
+                                  "attn_sink_fwd_decode", "attn_sink_fwd_decode_workspace_bytes", "attn_sink_merge",
                                   "attn_sink_status_string", "attn_sink_timing_enable", "attn_sink_timing_read"])
 
 
@@ -155,6 +155,29 @@ def test_fwd_decode_workspace(lib):
     assert lib.attn_sink_fwd_decode(ctypes.byref(s), *args[:6], FAKE, need - 1, None) == als.ERR_WORKSPACE
     assert lib.attn_sink_fwd_decode(ctypes.byref(s), *args[:6], None, need, None) == als.ERR_WORKSPACE
     assert lib.attn_sink_fwd_decode(ctypes.byref(s), *args[:6], FAKE + 8, need, None) == als.ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("args,status", [
+    ((als.BF16, 128, 8, 10, 2), als.ERR_UNSUPPORTED),
+    ((7, 64, 8, 10, 2), als.ERR_UNSUPPORTED),
+    ((als.BF16, 0, 8, 10, 2), als.ERR_INVALID_ARG),
+    ((als.BF16, 64, 0, 10, 2), als.ERR_INVALID_ARG),
+    ((als.BF16, 64, 8, -1, 2), als.ERR_INVALID_ARG),
+    ((als.BF16, 64, 8, 10, 0), als.ERR_INVALID_ARG),
+])
+def test_merge_rejects_bad_sizes(lib, args, status):
+    assert lib.attn_sink_merge(*args, FAKE, FAKE, FAKE, FAKE, FAKE, None) == status
+
+
+@pytest.mark.parametrize("slot", range(5))
+def test_merge_rejects_null_tensor(lib, slot):
+    ptrs = [FAKE] * 5
+    ptrs[slot] = None
+    assert lib.attn_sink_merge(als.FP32, 64, 8, 10, 3, *ptrs, None) == als.ERR_INVALID_ARG
+
+
+def test_merge_empty_is_a_no_op(lib):
+    assert lib.attn_sink_merge(als.FP32, 64, 8, 0, 3, None, None, FAKE, None, None, None) == als.OK
 
 
 def test_null_shape(lib):
