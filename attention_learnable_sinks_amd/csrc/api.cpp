@@ -71,7 +71,7 @@ attn_sink_status timed_launch(int kernel, hipStream_t stream, F&& launch) {
 attn_sink_status check_shape(const attn_sink_shape* s) {
   if (!s) return ATTN_SINK_ERR_INVALID_ARG;
   if (s->dtype != ATTN_SINK_BF16 && s->dtype != ATTN_SINK_FP32) return ATTN_SINK_ERR_UNSUPPORTED;
-  if (s->head_dim != kHeadDimBuilt) return s->head_dim > 0 ? ATTN_SINK_ERR_UNSUPPORTED : ATTN_SINK_ERR_INVALID_ARG;
+  if (!head_dim_built(s->head_dim)) return s->head_dim > 0 ? ATTN_SINK_ERR_UNSUPPORTED : ATTN_SINK_ERR_INVALID_ARG;
   if (s->num_heads_q < 1 || s->num_heads_kv < 1 || s->num_heads_q % s->num_heads_kv != 0)
     return ATTN_SINK_ERR_INVALID_ARG;
   if (s->num_seqs < 1 || s->total_q < 0 || s->total_k < 0 || s->max_seqlen_q < 0 || s->max_seqlen_k < 0)
@@ -85,11 +85,11 @@ attn_sink_status check_shape(const attn_sink_shape* s) {
   // Each kernel reads one head of one sequence through a buffer descriptor whose
   // byte range (rows x row pitch) must fit in 32 bits.
   const long long esize = s->dtype == ATTN_SINK_FP32 ? 4 : 2;
-  if ((long long)s->max_seqlen_q * s->num_heads_q * kHeadDimBuilt * esize >= (1LL << 32) ||
-      (long long)s->max_seqlen_k * s->num_heads_kv * kHeadDimBuilt * esize >= (1LL << 32))
+  if ((long long)s->max_seqlen_q * s->num_heads_q * s->head_dim * esize >= (1LL << 32) ||
+      (long long)s->max_seqlen_k * s->num_heads_kv * s->head_dim * esize >= (1LL << 32))
     return ATTN_SINK_ERR_UNSUPPORTED;
   // 32-bit row indices inside the kernels
-  if ((long long)s->total_q * s->num_heads_q * kHeadDimBuilt > 0x7fffffffLL * 4LL) return ATTN_SINK_ERR_UNSUPPORTED;
+  if ((long long)s->total_q * s->num_heads_q * s->head_dim > 0x7fffffffLL * 4LL) return ATTN_SINK_ERR_UNSUPPORTED;
   return ATTN_SINK_OK;
 }
 
@@ -114,12 +114,13 @@ FwdArgs fwd_args(const attn_sink_shape* s, const void* q, const void* k, const v
   a.scale = s->softmax_scale;
   a.causal = s->causal;
   a.window = s->window > 0 ? s->window : 0;
+  a.d = s->head_dim;
   return a;
 }
 
 DecodeWorkspace decode_layout(const attn_sink_shape* s) {
   return decode_workspace_layout(s->dtype == ATTN_SINK_FP32, s->num_heads_q, s->num_heads_kv, s->num_seqs,
-                                 s->max_seqlen_q, s->max_seqlen_k, s->window > 0 ? s->window : 0);
+                                 s->max_seqlen_q, s->max_seqlen_k, s->window > 0 ? s->window : 0, s->head_dim);
 }
 
 }  // namespace
@@ -176,7 +177,7 @@ attn_sink_status attn_sink_fwd_decode(const attn_sink_shape* shape, const void* 
 
 size_t attn_sink_bwd_workspace_bytes(const attn_sink_shape* shape) {
   if (check_shape(shape) != ATTN_SINK_OK) return 0;
-  return bwd_workspace_layout(shape->num_heads_q, shape->num_heads_kv, shape->total_q, shape->total_k, shape->num_seqs).total;
+  return bwd_workspace_layout(shape->num_heads_q, shape->num_heads_kv, shape->total_q, shape->total_k, shape->num_seqs, shape->head_dim).total;
 }
 
 attn_sink_status attn_sink_bwd(const attn_sink_shape* shape, const void* q, const void* k, const void* v,
@@ -189,7 +190,7 @@ attn_sink_status attn_sink_bwd(const attn_sink_shape* shape, const void* q, cons
   if (!sinks || !dsinks) return ATTN_SINK_ERR_INVALID_ARG;
   if (any_q && (!q || !o || !lse || !dout || !dq)) return ATTN_SINK_ERR_INVALID_ARG;
   if (any_k && (!k || !v || !dk || !dv)) return ATTN_SINK_ERR_INVALID_ARG;
-  const BwdWorkspace ws = bwd_workspace_layout(shape->num_heads_q, shape->num_heads_kv, shape->total_q, shape->total_k, shape->num_seqs);
+  const BwdWorkspace ws = bwd_workspace_layout(shape->num_heads_q, shape->num_heads_kv, shape->total_q, shape->total_k, shape->num_seqs, shape->head_dim);
   if (!workspace || workspace_bytes < ws.total || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
     return ATTN_SINK_ERR_WORKSPACE;
 
@@ -226,7 +227,7 @@ attn_sink_status attn_sink_merge(int dtype, int head_dim, int num_heads_q, int t
                                  const void* o_parts, const float* lse_parts, const float* sinks, void* o,
                                  float* lse, hipStream_t stream) {
   if (dtype != ATTN_SINK_BF16 && dtype != ATTN_SINK_FP32) return ATTN_SINK_ERR_UNSUPPORTED;
-  if (head_dim != kHeadDimBuilt) return head_dim > 0 ? ATTN_SINK_ERR_UNSUPPORTED : ATTN_SINK_ERR_INVALID_ARG;
+  if (!head_dim_built(head_dim)) return head_dim > 0 ? ATTN_SINK_ERR_UNSUPPORTED : ATTN_SINK_ERR_INVALID_ARG;
   if (num_heads_q < 1 || total_q < 0 || num_parts < 1) return ATTN_SINK_ERR_INVALID_ARG;
   if (!sinks) return ATTN_SINK_ERR_INVALID_ARG;
   if (total_q > 0 && (!o_parts || !lse_parts || !o || !lse)) return ATTN_SINK_ERR_INVALID_ARG;
@@ -240,6 +241,7 @@ attn_sink_status attn_sink_merge(int dtype, int head_dim, int num_heads_q, int t
   a.parts = num_parts;
   a.hq = num_heads_q;
   a.total_q = total_q;
+  a.d = head_dim;
   const int fp32 = dtype == ATTN_SINK_FP32;
   return timed_launch(K_MERGE, stream, [&] { return launch_merge(a, fp32, stream); });
 }

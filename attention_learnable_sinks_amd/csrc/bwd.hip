@@ -39,21 +39,21 @@ namespace attn_sink {
 constexpr int kPreRows = 64;  // rows per bwd_pre workgroup
 
 // ----------------------------------------------------------------------------- 1. preprocess
-template <typename T>
+template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   const FwdArgs& f = a.f;
   const int head = blockIdx.y;
   const int tid = threadIdx.x;
   const int row = blockIdx.x * kPreRows + tid / 4;
-  const int part = tid % 4;  // 16 of the 64 columns
+  const int part = tid % 4;  // a quarter of the D columns
   float contrib = 0.f;
   if (row < f.total_q) {
-    const size_t base = ((size_t)row * f.hq + head) * kD + part * 16;
+    const size_t base = ((size_t)row * f.hq + head) * D + part * (D / 4);
     const T* o = static_cast<const T*>(f.o) + base;
     const T* d = static_cast<const T*>(a.dout) + base;
     float acc = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc += to_f32(o[e]) * to_f32(d[e]);
+    for (int e = 0; e < D / 4; ++e) acc += to_f32(o[e]) * to_f32(d[e]);
     acc += __shfl_xor(acc, 1);
     acc += __shfl_xor(acc, 2);
     if (part == 0) {
@@ -75,17 +75,17 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 }
 
 // ----------------------------------------------------------------------------- 2. dQ
-template <typename T>
+template <typename T, int D>
 struct DqCfg {
   static constexpr int BM = 128;  // query rows per workgroup (4 wavefronts x 32)
   static constexpr int BN = 64;   // keys per tile
   static constexpr int THREADS = 256;
-  static constexpr int TILE = tile_elems<T>(BN);
+  static constexpr int TILE = tile_elems_d<T, D>(BN);
 };
 
-template <typename T>
+template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
-  using C = DqCfg<T>;
+  using C = DqCfg<T, D>;
   using M = Mfma<T>;
   constexpr int E = M::E, KS = M::KS;
   const FwdArgs& f = a.f;
@@ -115,22 +115,22 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   int wlo = f.window > 0 ? clampi(qw + off - f.window + 1, 0, nk) : 0;
   if (qw >= nq) whi = wlo = 0;
 
-  const size_t kv_row = (size_t)f.hkv * kD, q_row = (size_t)f.hq * kD;
-  const T* kbase_p = static_cast<const T*>(f.k) + (size_t)sk.start * kv_row + g * kD;
-  const T* vbase_p = static_cast<const T*>(f.v) + (size_t)sk.start * kv_row + g * kD;
+  const size_t kv_row = (size_t)f.hkv * D, q_row = (size_t)f.hq * D;
+  const T* kbase_p = static_cast<const T*>(f.k) + (size_t)sk.start * kv_row + g * D;
+  const T* vbase_p = static_cast<const T*>(f.v) + (size_t)sk.start * kv_row + g * D;
 
   // Q and dO fragments (B operands of S^T = K Q^T and dP^T = V dO^T); lse and D of the lane's row.
   const int qi = qw + c;
   const bool qok = qi < nq;
   Span row_keys = keys_of_row(qi, off, nk, f.causal, f.window);  // the keys row qi sees
   if (!qok) row_keys.len = 0u;
-  typename M::Frag qf[kD / KS], dof[kD / KS];
+  typename M::Frag qf[D / KS], dof[D / KS];
   {
-    const size_t o = ((size_t)(sq.start + (qok ? qi : 0)) * f.hq + head) * kD;
+    const size_t o = ((size_t)(sq.start + (qok ? qi : 0)) * f.hq + head) * D;
     const T* qsrc = static_cast<const T*>(f.q) + o;
     const T* dsrc = static_cast<const T*>(a.dout) + o;
 #pragma unroll
-    for (int s = 0; s < kD / KS; ++s) {
+    for (int s = 0; s < D / KS; ++s) {
       qf[s] = global_frag<T>(qsrc + KS * s + E * h, qok);
       dof[s] = global_frag<T>(dsrc + KS * s + E * h, qok);
     }
@@ -142,15 +142,15 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) neg_dd[r] = -dd;
 
-  f32x16 dqt[2];  // dQ^T [64 d x 32 q]
+  f32x16 dqt[D / 32];  // dQ^T [D x 32 q]
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < D / 32; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqt[t][r] = 0.f;
 
   const int kt_begin = klo / C::BN;
   const int kt_end = khi > klo ? (khi + C::BN - 1) / C::BN : kt_begin;
-  TileLoader<T, C::BN, C::THREADS> kld, vld;
+  TileLoaderD<T, C::BN, C::THREADS, D> kld, vld;
   kld.init(kbase_p, kv_row, nk, tid);
   vld.init(vbase_p, kv_row, nk, tid);
   if (kt_begin < kt_end) {
@@ -177,13 +177,14 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
         dpt[mt][r] = 0.f;
       }
 #pragma unroll
-      for (int s = 0; s < kD / KS; ++s) {
-        st[mt] = M::mma(fa.row(Ks, mt, s), qf[s], st[mt]);
+      for (int s = 0; s < D / KS; ++s) {
+        st[mt] = M::mma(frag_row<T, C::BN>(fa, Ks, mt, s), qf[s], st[mt]);
+        const auto vfr = frag_row<T, C::BN>(fa, Vs, mt, s);
         if constexpr (sizeof(T) == 2) {
           // bf16: dP^T starts from -D (a loop-invariant seed), so it ends at dP^T - D.
-          dpt[mt] = s == 0 ? mma_seeded(fa.row(Vs, mt, s), dof[s], neg_dd) : M::mma(fa.row(Vs, mt, s), dof[s], dpt[mt]);
+          dpt[mt] = s == 0 ? mma_seeded(vfr, dof[s], neg_dd) : M::mma(vfr, dof[s], dpt[mt]);
         } else {
-          dpt[mt] = M::mma(fa.row(Vs, mt, s), dof[s], dpt[mt]);
+          dpt[mt] = M::mma(vfr, dof[s], dpt[mt]);
         }
       }
     }
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     for (int s = 0; s < C::BN / KS; ++s) {
       const typename M::Frag sf = pack_frag<T>(st, s);
 #pragma unroll
-      for (int md = 0; md < 2; ++md) dqt[md] = M::mma(fa.col(Ks, md, s), sf, dqt[md]);
+      for (int md = 0; md < D / 32; ++md) dqt[md] = M::mma(frag_col<T, C::BN>(fa, Ks, md, s), sf, dqt[md]);
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -243,9 +244,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   for (; kt < kt_end; ++kt) step(kt, std::false_type{});
 
   if (qok) {
-    T* dst = static_cast<T*>(a.dq) + (size_t)(sq.start + qi) * q_row + head * kD;
+    T* dst = static_cast<T*>(a.dq) + (size_t)(sq.start + qi) * q_row + head * D;
 #pragma unroll
-    for (int md = 0; md < 2; ++md)
+    for (int md = 0; md < D / 32; ++md)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d0 = 32 * md + crow(4 * r4, h);
@@ -263,24 +264,26 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ----------------------------------------------------------------------------- 3. dK, dV
-template <typename T>
+template <typename T, int D>
 struct DkvCfg {
   static constexpr int BMB = 64;   // queries per tile
   static constexpr int BNB = 128;  // keys per key tile (4 wavefronts x 32)
   static constexpr int THREADS = 256;
-  static constexpr int TILE = tile_elems<T>(BMB);
+  static constexpr int TILE = tile_elems_d<T, D>(BMB);
 };
 
-template <typename T>
-__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a) {
-  using C = DkvCfg<T>;
+template <typename T, int D>
+__global__ __launch_bounds__(256, (sizeof(T) == 2 && D == 64) ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a) {
+  using C = DkvCfg<T, D>;
   using M = Mfma<T>;
   constexpr int E = M::E, KS = M::KS;
   const FwdArgs& f = a.f;
   // bf16 stages tiles two steps ahead (three buffers); fp32 stages through registers, one ahead.
   constexpr int NB = sizeof(T) == 2 ? 3 : 2;
-  static_assert(sizeof(T) != 2 || TileLoader<bf16, C::BMB, C::THREADS>::N == 2,
-                "the vmcnt counts in step() assume two DMA instructions per tile and wavefront");
+  using QLoader = TileLoaderD<T, C::BMB, C::THREADS, D>;
+  // bf16: this wavefront's DMA instructions per staged tile (Q and dO; waves 0 and 1
+  // add one row-statistics load), for the waits in step().
+  constexpr int kStageVm = 2 * QLoader::N;
   __shared__ __attribute__((aligned(16))) T smem[NB * 2 * C::TILE];  // [buf][Q, dO]
   __shared__ __attribute__((aligned(16))) float lse2_s[NB][C::BMB];
   __shared__ __attribute__((aligned(16))) float dd_s[NB][C::BMB];
@@ -302,7 +305,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
   const int h = lane >> 5, c = lane & 31;
   FragAddr<T> fa;
   fa.init(lane);
-  const size_t kv_row = (size_t)f.hkv * kD, q_row = (size_t)f.hq * kD;
+  const size_t kv_row = (size_t)f.hkv * D, q_row = (size_t)f.hq * D;
   const float sl2 = f.scale * kLog2e;
   const T* qhead_p = static_cast<const T*>(f.q) + (size_t)sq.start * q_row;
   const T* dohead_p = static_cast<const T*>(a.dout) + (size_t)sq.start * q_row;
@@ -328,27 +331,27 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
     const int kj = kw + c;
     const bool kok = kj < nk;
     const Span key_rows = rows_of_key(kj, off, nq, nk, f.causal, f.window);  // the rows that see key kj
-    typename M::Frag kf[kD / KS], vf[kD / KS];
+    typename M::Frag kf[D / KS], vf[D / KS];
     {
-      const size_t o = (size_t)(sk.start + (kok ? kj : 0)) * kv_row + g * kD;
+      const size_t o = (size_t)(sk.start + (kok ? kj : 0)) * kv_row + g * D;
       const T* ksrc = static_cast<const T*>(f.k) + o;
       const T* vsrc = static_cast<const T*>(f.v) + o;
 #pragma unroll
-      for (int s = 0; s < kD / KS; ++s) {
+      for (int s = 0; s < D / KS; ++s) {
         kf[s] = global_frag<T>(ksrc + KS * s + E * h, kok);
         vf[s] = global_frag<T>(vsrc + KS * s + E * h, kok);
       }
     }
-    f32x16 dkt[2], dvt[2];  // dK^T, dV^T: [64 d x 32 keys]
+    f32x16 dkt[D / 32], dvt[D / 32];  // dK^T, dV^T: [D x 32 keys]
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < D / 32; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         dkt[t][r] = 0.f;
         dvt[t][r] = 0.f;
       }
 
-    TileLoader<T, C::BMB, C::THREADS> qld, dold;
+    QLoader qld, dold;
     RowLoader lld, dld;  // the tile's lse * log2(e) and -D rows (waves 0 and 1)
     int staged_head = -1;
     // Start moving (head, query tile) of iteration `it` into LDS buffer `buf`.
@@ -356,8 +359,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
       const int hd = head0 + it / nqt;
       const int qt = qt_begin + it % nqt;
       if (hd != staged_head) {  // uniform: new descriptors when the query head changes
-        qld.init(qhead_p + hd * kD, q_row, nq, tid);
-        dold.init(dohead_p + hd * kD, q_row, nq, tid);
+        qld.init(qhead_p + hd * D, q_row, nq, tid);
+        dold.init(dohead_p + hd * D, q_row, nq, tid);
         lld.init(a.rowstat + (size_t)(2 * hd) * f.total_q + sq.start, nq);
         dld.init(a.rowstat + (size_t)(2 * hd + 1) * f.total_q + sq.start, nq);
         staged_head = hd;
@@ -410,15 +413,15 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
         // All operands of this block's 8 MFMAs are read first; the scheduling barrier
         // keeps the reads from being sunk next to their MFMAs (which would expose the
         // LDS latency once per MFMA).
-        typename M::Frag qa[kD / KS], da[kD / KS];
+        typename M::Frag qa[D / KS], da[D / KS];
 #pragma unroll
-        for (int s = 0; s < kD / KS; ++s) {
-          qa[s] = fa.row(Qs, mq, s);
-          da[s] = fa.row(dOs, mq, s);
+        for (int s = 0; s < D / KS; ++s) {
+          qa[s] = frag_row<T, C::BMB>(fa, Qs, mq, s);
+          da[s] = frag_row<T, C::BMB>(fa, dOs, mq, s);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int s = 0; s < kD / KS; ++s) {
+        for (int s = 0; s < D / KS; ++s) {
           pt[mq] = M::mma(qa[s], kf[s], pt[mq]);
           if constexpr (sizeof(T) == 2)
             dst[mq] = s == 0 ? mma_seeded(da[s], vf[s], seed) : M::mma(da[s], vf[s], dst[mq]);
@@ -452,9 +455,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
         const typename M::Frag pf = pack_frag<T>(pt, s);
         const typename M::Frag sf = pack_frag<T>(dst, s);
 #pragma unroll
-        for (int md = 0; md < 2; ++md) {
-          dvt[md] = M::mma(fa.col(dOs, md, s), pf, dvt[md]);
-          dkt[md] = M::mma(fa.col(Qs, md, s), sf, dkt[md]);
+        for (int md = 0; md < D / 32; ++md) {
+          dvt[md] = M::mma(frag_col<T, C::BMB>(fa, dOs, md, s), pf, dvt[md]);
+          dkt[md] = M::mma(frag_col<T, C::BMB>(fa, Qs, md, s), sf, dkt[md]);
         }
       }
     };
@@ -472,15 +475,16 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
         if (wave_keys && qbase < wqhi && qlast >= wqlo) body(buf, qbase, full_tag);
       }
       if constexpr (NB == 3) {
-        // Tile it+1 must have landed; tile it+2's DMAs (this wavefront's last 4 or 5
-        // vector-memory instructions, the lse / -D row on waves 0 and 1) may still fly.
+        // Tile it+1 must have landed; tile it+2's DMAs (this wavefront's last
+        // kStageVm vector-memory instructions, plus the lse / -D row on waves 0 and
+        // 1) may still fly.
         if (more) {
           if (w < 2)
-            __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5)
+            wait_vmcnt<kStageVm + 1>();
           else
-            __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+            wait_vmcnt<kStageVm>();
         } else {
-          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+          wait_vmcnt<0>();
         }
       } else {
         if (more) commit((it + 1) % NB);
@@ -507,9 +511,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
 
     // Lane owns key kj; register r of tile md holds d = 32 md + crow(r, h).
     if (kok) {
-      const size_t o = (size_t)(sk.start + kj) * kv_row + g * kD;
+      const size_t o = (size_t)(sk.start + kj) * kv_row + g * D;
 #pragma unroll
-      for (int md = 0; md < 2; ++md)
+      for (int md = 0; md < D / 32; ++md)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int d0 = 32 * md + crow(4 * r4, h);
@@ -536,6 +540,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(B
 // ----------------------------------------------------------------------------- 4. finish
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_finish_kernel(BwdArgs a) {
+  const int D = a.f.d;
   const FwdArgs& f = a.f;
   if ((int)blockIdx.x < f.hq) {
     // dS_h of head blockIdx.x: the preprocess partials, summed in a fixed order
@@ -551,7 +556,7 @@ __global__ __launch_bounds__(256) void bwd_finish_kernel(BwdArgs a) {
     if (threadIdx.x == 0) a.dsinks[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
   }
   if (a.splits > 1) {
-    const size_t n4 = (size_t)f.total_k * f.hkv * kD / 4;
+    const size_t n4 = (size_t)f.total_k * f.hkv * D / 4;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x) {
       f32x4 sk = reinterpret_cast<const f32x4*>(a.dk_part)[i];
       f32x4 sv = reinterpret_cast<const f32x4*>(a.dv_part)[i];
@@ -597,7 +602,7 @@ int bwd_head_splits(int hq, int hkv, int total_k, int num_seqs) {
   return best;
 }
 
-BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k, int num_seqs) {
+BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k, int num_seqs, int d) {
   BwdWorkspace w;
   const int rows = total_q > 0 ? total_q : 1;
   w.pre_blocks = (rows + kPreRows - 1) / kPreRows;
@@ -605,7 +610,7 @@ BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k, int
   size_t o = 0;
   w.rowstat = o;     o = align256(o + (size_t)hq * 2 * total_q * 4);
   w.dsink_part = o;  o = align256(o + (size_t)hq * w.pre_blocks * 4);
-  const size_t part = w.splits > 1 ? (size_t)w.splits * total_k * hkv * kD * 4 : 0;
+  const size_t part = w.splits > 1 ? (size_t)w.splits * total_k * hkv * d * 4 : 0;
   w.dk_part = o;     o = align256(o + part);
   w.dv_part = o;     o = align256(o + part);
   w.total = o;
@@ -614,39 +619,60 @@ BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k, int
 
 hipError_t launch_bwd_pre(const BwdArgs& a, int fp32, hipStream_t stream) {
   dim3 grid(a.pre_blocks, a.f.hq);
-  if (fp32)
-    hipLaunchKernelGGL(bwd_pre_kernel<float>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(bwd_pre_kernel<bf16>, grid, dim3(256), 0, stream, a);
+  if (a.f.d == 128) {
+    if (fp32)
+      hipLaunchKernelGGL((bwd_pre_kernel<float, 128>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_pre_kernel<bf16, 128>), grid, dim3(256), 0, stream, a);
+  } else {
+    if (fp32)
+      hipLaunchKernelGGL((bwd_pre_kernel<float, 64>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_pre_kernel<bf16, 64>), grid, dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, int fp32, hipStream_t stream) {
-  const int tiles = (a.f.max_q + DqCfg<bf16>::BM - 1) / DqCfg<bf16>::BM;
+  const int tiles = (a.f.max_q + DqCfg<bf16, 64>::BM - 1) / DqCfg<bf16, 64>::BM;
   if (tiles == 0) return hipSuccess;
   dim3 grid(a.f.hq * a.f.num_seqs, tiles);
-  if (fp32)
-    hipLaunchKernelGGL(bwd_dq_kernel<float>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(bwd_dq_kernel<bf16>, grid, dim3(256), 0, stream, a);
+  if (a.f.d == 128) {
+    if (fp32)
+      hipLaunchKernelGGL((bwd_dq_kernel<float, 128>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<bf16, 128>), grid, dim3(256), 0, stream, a);
+  } else {
+    if (fp32)
+      hipLaunchKernelGGL((bwd_dq_kernel<float, 64>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<bf16, 64>), grid, dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int fp32, hipStream_t stream) {
-  const int ktiles = (a.f.max_k + DkvCfg<bf16>::BNB - 1) / DkvCfg<bf16>::BNB;
+  const int ktiles = (a.f.max_k + DkvCfg<bf16, 64>::BNB - 1) / DkvCfg<bf16, 64>::BNB;
   if (ktiles == 0) return hipSuccess;
   dim3 grid(a.f.hkv * a.splits * a.f.num_seqs, (ktiles + 1) / 2);
-  if (fp32)
-    hipLaunchKernelGGL(bwd_dkdv_kernel<float>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(bwd_dkdv_kernel<bf16>, grid, dim3(256), 0, stream, a);
+  if (a.f.d == 128) {
+    if (fp32)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<float, 128>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<bf16, 128>), grid, dim3(256), 0, stream, a);
+  } else {
+    if (fp32)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<float, 64>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<bf16, 64>), grid, dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_finish(const BwdArgs& a, int fp32, hipStream_t stream) {
   size_t blocks = 1;
   if (a.splits > 1) {
-    const size_t n4 = (size_t)a.f.total_k * a.f.hkv * kD / 4;
+    const size_t n4 = (size_t)a.f.total_k * a.f.hkv * a.f.d / 4;
     blocks = (n4 + 255) / 256;
     if (blocks > 4096) blocks = 4096;
     if (blocks == 0) blocks = 1;

@@ -29,7 +29,7 @@
 
 namespace attn_sink {
 
-constexpr int kD = 64;  // head dim (the only one built)
+constexpr int kD = 64;  // columns of one LDS tile block; head dims are multiples of it (64, 128)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -101,6 +101,14 @@ struct Tile<float> {
 template <typename T>
 constexpr int tile_elems(int rows) {
   return rows * Tile<T>::ELEMS_PER_ROW;
+}
+
+// A tile of D columns (D = 64 or 128) is stored as D / 64 consecutive 64-column
+// blocks, each a `rows` x 64 tile in the layout above, so every operand read and
+// DMA pattern stays that of the 64-column tile.
+template <typename T, int D>
+constexpr int tile_elems_d(int rows) {
+  return (D / kD) * tile_elems<T>(rows);
 }
 
 // Operand whose lane holds row `row` and k-slots [col, col + E) of a tile
@@ -191,6 +199,19 @@ struct FragAddr<float> {
     return lds_col_frag<float>(tile, 32 * md, s, lane_, true);
   }
 };
+
+// The two fragment kinds on a tile of ROWS rows and D columns (tile_elems_d): step s
+// of the contraction over the columns (row fragments) or column block md of 32
+// (transposed fragments) picks its 64-column block at a compile-time offset.
+template <typename T, int ROWS>
+__device__ inline typename Mfma<T>::Frag frag_row(const FragAddr<T>& fa, const T* tile, int mt, int s) {
+  constexpr int PER = kD / Mfma<T>::KS;  // steps per 64-column block
+  return fa.row(tile + (s / PER) * tile_elems<T>(ROWS), mt, s % PER);
+}
+template <typename T, int ROWS>
+__device__ inline typename Mfma<T>::Frag frag_col(const FragAddr<T>& fa, const T* tile, int md, int s) {
+  return fa.col(tile + (md / 2) * tile_elems<T>(ROWS), md % 2, s);
+}
 
 // acc += A B (bf16, 32x32x16) with the accumulator held in AGPRs.  Accumulators
 // that the vector ALUs never touch inside a loop (O, dQ, dK, dV) live there so the
@@ -337,6 +358,15 @@ __device__ inline void lds_dma_b32(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, u
 // for the asm tile DMAs in flight.
 __device__ inline void vmem_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
+// Wait until at most N of this wavefront's vector-memory instructions are in flight
+// (N < 64), as asm with a memory clobber: the compiler neither moves memory accesses
+// across it nor knows of the asm DMAs it waits for.
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Tile loader with one interface for both element types: issue(row0, tile) starts
 // moving rows [row0, row0 + ROWS) of the head into LDS tile `tile`, finish() makes
 // sure they have arrived (the caller then synchronises the workgroup).
@@ -381,6 +411,7 @@ struct TileLoader<bf16, ROWS, THREADS> {
 
 template <int ROWS, int THREADS>
 struct TileLoader<float, ROWS, THREADS> {
+  static constexpr int N = Stager<float, ROWS, THREADS>::N;  // register loads per thread
   Stager<float, ROWS, THREADS> st;
   float* dst;
   int tid_;
@@ -393,6 +424,28 @@ struct TileLoader<float, ROWS, THREADS> {
     dst = tile;
   }
   __device__ inline void finish() { st.store(dst, tid_); }
+};
+
+// A tile of ROWS rows and D columns of one head (tile_elems_d layout): one 64-column
+// loader per column block.  N: vector-memory instructions per thread and tile.
+template <typename T, int ROWS, int THREADS, int D>
+struct TileLoaderD {
+  using Sub = TileLoader<T, ROWS, THREADS>;
+  static constexpr int BLOCKS = D / kD;
+  static constexpr int N = BLOCKS * Sub::N;
+  Sub sub[BLOCKS];
+  __device__ inline void init(const T* base, size_t row_stride, int nrows, int tid) {
+#pragma unroll
+    for (int i = 0; i < BLOCKS; ++i) sub[i].init(base + kD * i, row_stride, nrows, tid);
+  }
+  __device__ inline void issue(int row0, T* tile) {
+#pragma unroll
+    for (int i = 0; i < BLOCKS; ++i) sub[i].issue(row0, tile + i * tile_elems<T>(ROWS));
+  }
+  __device__ inline void finish() {
+#pragma unroll
+    for (int i = 0; i < BLOCKS; ++i) sub[i].finish();
+  }
 };
 
 // 64 consecutive floats of one row-statistics array moved straight into LDS by one

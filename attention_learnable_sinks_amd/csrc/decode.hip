@@ -68,14 +68,15 @@ __device__ inline TileRange visible_tiles(int nq, int nk, int causal, int window
   return {klo / kDecBN, (khi + kDecBN - 1) / kDecBN};
 }
 
-template <typename T>
+// D: head dim (64 or 128).
+template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
   using M = Mfma<T>;
   using Frag = typename M::Frag;
   constexpr int E = M::E, KS = M::KS;
-  constexpr int NQ = kD / KS;      // operand steps over the head dim
+  constexpr int NQ = D / KS;       // operand steps over the head dim
   constexpr int NP = kDecBN / KS;  // operand steps over the keys of a tile
-  constexpr int TILE = tile_elems<T>(kDecBN);
+  constexpr int TILE = tile_elems_d<T, D>(kDecBN);
   constexpr int STAGES = dec_stages<T>();
   constexpr int MT = kDecBN / 32;  // 32-key blocks per tile
   __shared__ __attribute__((aligned(16))) T smem[kDecWaves * STAGES * 2 * TILE];
@@ -111,26 +112,26 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
   Frag qf[NQ];
   auto load_q = [&]() __attribute__((always_inline)) {
     const T* src = static_cast<const T*>(f.q) + ((size_t)(sq.start + (col_ok ? col_row : 0)) * f.hq +
-                                                 (col_ok ? col_head : 0)) * kD;
+                                                 (col_ok ? col_head : 0)) * D;
 #pragma unroll
     for (int s = 0; s < NQ; ++s) qf[s] = global_frag<T>(src + KS * s + E * h, col_ok);
     vmem_drain();  // the Q loads (and anything issued before them) are done
   };
   const float sl2 = f.scale * kLog2e;
   float m_run = -INFINITY, l_run = 0.f;
-  f32x16 oacc[2];
+  f32x16 oacc[D / 32];  // O^T: [D x 32 columns]
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < D / 32; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[t][r] = 0.f;
 
-  const size_t kv_row = (size_t)f.hkv * kD;
+  const size_t kv_row = (size_t)f.hkv * D;
   T* const stage0 = smem + w * STAGES * 2 * TILE;  // [stage][K, V]
   FragAddr<T> fa;
   fa.init(lane);
-  TileLoader<T, kDecBN, 64> kld, vld;  // each wavefront moves its own tiles
-  kld.init(static_cast<const T*>(f.k) + (size_t)sk.start * kv_row + g * kD, kv_row, nk, lane);
-  vld.init(static_cast<const T*>(f.v) + (size_t)sk.start * kv_row + g * kD, kv_row, nk, lane);
+  TileLoaderD<T, kDecBN, 64, D> kld, vld;  // each wavefront moves its own tiles
+  kld.init(static_cast<const T*>(f.k) + (size_t)sk.start * kv_row + g * D, kv_row, nk, lane);
+  vld.init(static_cast<const T*>(f.v) + (size_t)sk.start * kv_row + g * D, kv_row, nk, lane);
 
   // One key tile against the 32 columns: scores, mask, online softmax, P V.
   auto tile = [&](int t, const T* Ks, const T* Vs) __attribute__((always_inline)) {
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[mt][r] = 0.f;
 #pragma unroll
-      for (int s = 0; s < NQ; ++s) st[mt] = M::mma(fa.row(Ks, mt, s), qf[s], st[mt]);
+      for (int s = 0; s < NQ; ++s) st[mt] = M::mma(frag_row<T, kDecBN>(fa, Ks, mt, s), qf[s], st[mt]);
     }
     // Mask to the column's visible keys (key of register r: t*BN + 4h + 32mt + 8(r/4) + r%4).
     const int k0 = t * kDecBN + 4 * h;
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
     const float neg_m = m_new == -INFINITY ? 0.f : -m_new;
     l_run *= alpha;
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
+    for (int t2 = 0; t2 < D / 32; ++t2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[t2][r] *= alpha;
     m_run = m_new;
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
       const Frag pf = pack_frag<T>(st, s);
       l_run = frag_sum<T>(pf, l_run);  // the sum of the rounded P that multiplies V
 #pragma unroll
-      for (int md = 0; md < 2; ++md) oacc[md] = M::mma(fa.col(Vs, md, s), pf, oacc[md]);
+      for (int md = 0; md < D / 32; ++md) oacc[md] = M::mma(frag_col<T, kDecBN>(fa, Vs, md, s), pf, oacc[md]);
     }
   };
 
@@ -195,15 +196,15 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
       if (t + STAGES - 1 < t1) issue(t + STAGES - 1, stage(i + STAGES - 1));
       // Wait until tile t has landed: allow the DMAs of the tiles issued after it.
       const int ahead = min(STAGES - 1, t1 - 1 - t);
-      static_assert(STAGES <= 4 && PER_TILE == 8, "wait counts below");
+      static_assert(STAGES <= 4 && 3 * PER_TILE < 64, "wait counts below");
       if (ahead >= 3)
-        asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+        wait_vmcnt<3 * PER_TILE>();
       else if (ahead == 2)
-        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        wait_vmcnt<2 * PER_TILE>();
       else if (ahead == 1)
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        wait_vmcnt<PER_TILE>();
       else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        wait_vmcnt<0>();
       const T* const cur = stage(i);
       tile(t, cur, cur + TILE);
     }
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
       vld.issue(t * kDecBN, stage0 + TILE);
       kld.finish();
       vld.finish();
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      wait_vmcnt<0>();
       tile(t, stage0, stage0 + TILE);
     }
   }
@@ -232,9 +233,9 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
       l_tot = l_col * o_sc + (sink2 > -INFINITY ? fast_exp2(sink2 - mm) : 0.f);
     }
     const float inv = l_tot > 0.f ? o_sc / l_tot : 0.f;
-    T* dst = static_cast<T*>(f.o) + ((size_t)(sq.start + col_row) * f.hq + col_head) * kD;
+    T* dst = static_cast<T*>(f.o) + ((size_t)(sq.start + col_row) * f.hq + col_head) * D;
 #pragma unroll
-    for (int md = 0; md < 2; ++md)
+    for (int md = 0; md < D / 32; ++md)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d0 = 32 * md + crow(4 * r4, h);
@@ -255,9 +256,9 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
   }
   // Partial of this chunk: column slot c of (sequence, kv head, chunk).
   const size_t slot = ((size_t)(b * f.hkv + g) * a.max_chunks + ci) * a.cols + c;
-  float* po = a.part_o + slot * kD;
+  float* po = a.part_o + slot * D;
 #pragma unroll
-  for (int md = 0; md < 2; ++md)
+  for (int md = 0; md < D / 32; ++md)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int d0 = 32 * md + crow(4 * r4, h);
@@ -268,9 +269,11 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
 }
 
 // One workgroup per (sequence, kv head); a wavefront per column (query head, new
-// row), lane = d.  The column's chunk statistics are wavefront-uniform (scalar loads).
-template <typename T>
+// row), lane = d (and d + 64 when D = 128).  The column's chunk statistics are
+// wavefront-uniform.
+template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int DL = D / 64;  // values of d per lane
   const FwdArgs& f = a.f;
   const int b = blockIdx.x / f.hkv, g = blockIdx.x % f.hkv;
   const int G = f.hq / f.hkv;
@@ -286,22 +289,25 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   for (int cc = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); cc < ncols; cc += nw) {
     const int row = cc / G, head = g * G + cc % G;
     const float* ml = a.part_ml + 2 * (base + cc);      // chunk ch at 2 * ch * cols
-    const float* po = a.part_o + (base + cc) * kD + d;  // chunk ch at ch * cols * 64
-    const size_t mstride = 2 * (size_t)a.cols, ostride = (size_t)a.cols * kD;
+    const float* po = a.part_o + (base + cc) * D + d;  // chunk ch at ch * cols * D
+    const size_t mstride = 2 * (size_t)a.cols, ostride = (size_t)a.cols * D;
     // Running (max M, sum l, output o), seeded with the sink's mass; chunks are
     // merged in order, U at a time: the U chunks' values are loaded together (one
     // round trip), then folded in.
     const float sink2 = f.sinks[head] * kLog2e;
-    float mm = sink2, l = sink2 > -INFINITY ? 1.f : 0.f, o = 0.f;
+    float mm = sink2, l = sink2 > -INFINITY ? 1.f : 0.f, o[DL];
+#pragma unroll
+    for (int j = 0; j < DL; ++j) o[j] = 0.f;
     constexpr int U = 16;
     for (int c0 = 0; c0 < nchunks; c0 += U) {
-      float ms[U], ls[U], os[U];
+      float ms[U], ls[U], os[U][DL];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const bool ok = c0 + u < nchunks;
         ms[u] = ok ? ml[(c0 + u) * mstride] : -INFINITY;
         ls[u] = ok ? ml[(c0 + u) * mstride + 1] : 0.f;
-        os[u] = ok ? po[(c0 + u) * ostride] : 0.f;
+#pragma unroll
+        for (int j = 0; j < DL; ++j) os[u][j] = ok ? po[(c0 + u) * ostride + 64 * j] : 0.f;
       }
       float bm = mm;
 #pragma unroll
@@ -309,25 +315,30 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
       if (bm == -INFINITY) continue;  // nothing seen yet, no sink
       const float sc = mm == -INFINITY ? 0.f : fast_exp2(mm - bm);
       l *= sc;
-      o *= sc;
+#pragma unroll
+      for (int j = 0; j < DL; ++j) o[j] *= sc;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         // a chunk in which this row sees no key has ms = -inf, l = 0, O = 0
         const float e = ms[u] == -INFINITY ? 0.f : fast_exp2(ms[u] - bm);
         l += ls[u] * e;
-        o += os[u] * e;
+#pragma unroll
+        for (int j = 0; j < DL; ++j) o[j] += os[u][j] * e;
       }
       mm = bm;
     }
     const size_t orow = (size_t)(sq.start + row) * f.hq + head;
-    static_cast<T*>(f.o)[orow * kD + d] = from_f32<T>(l > 0.f ? o / l : 0.f);
+#pragma unroll
+    for (int j = 0; j < DL; ++j)
+      static_cast<T*>(f.o)[orow * D + d + 64 * j] = from_f32<T>(l > 0.f ? o[j] / l : 0.f);
     if (d == 0) f.lse[(size_t)head * f.total_q + sq.start + row] = l > 0.f ? (mm + fast_log2(l)) * kLn2 : -INFINITY;
   }
 }
 
 bool decode_supported(int hq, int hkv, int max_q) { return (long long)(hq / hkv) * max_q <= kDecCols; }
 
-DecodeWorkspace decode_workspace_layout(int fp32, int hq, int hkv, int num_seqs, int max_q, int max_k, int window) {
+DecodeWorkspace decode_workspace_layout(int fp32, int hq, int hkv, int num_seqs, int max_q, int max_k, int window,
+                                        int d) {
   DecodeWorkspace w;
   (void)fp32;
   // kv heads per workgroup: the largest divisor of hkv up to kDecWaves.
@@ -352,7 +363,7 @@ DecodeWorkspace decode_workspace_layout(int fp32, int hq, int hkv, int num_seqs,
   if (w.cols < 1) w.cols = 1;
   const size_t parts = w.max_chunks > 1 ? (size_t)num_seqs * hkv * w.max_chunks * w.cols : 0;
   w.part_o = 0;
-  w.part_ml = (parts * kD * sizeof(float) + 255) & ~(size_t)255;
+  w.part_ml = (parts * d * sizeof(float) + 255) & ~(size_t)255;
   w.total = w.part_ml + ((parts * 2 * sizeof(float) + 255) & ~(size_t)255);
   if (w.total == 0) w.total = 256;  // nothing to keep, but a valid shape never reports 0
   return w;
@@ -361,20 +372,34 @@ DecodeWorkspace decode_workspace_layout(int fp32, int hq, int hkv, int num_seqs,
 hipError_t launch_decode_partial(const DecodeArgs& a, int fp32, hipStream_t stream) {
   dim3 grid(a.f.num_seqs * (a.f.hkv / a.hw), a.max_chunks);
   dim3 block(64 * a.hw);
-  if (fp32)
-    hipLaunchKernelGGL(decode_partial_kernel<float>, grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL(decode_partial_kernel<bf16>, grid, block, 0, stream, a);
+  if (a.f.d == 128) {
+    if (fp32)
+      hipLaunchKernelGGL((decode_partial_kernel<float, 128>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_partial_kernel<bf16, 128>), grid, block, 0, stream, a);
+  } else {
+    if (fp32)
+      hipLaunchKernelGGL((decode_partial_kernel<float, 64>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_partial_kernel<bf16, 64>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_decode_merge(const DecodeArgs& a, int fp32, hipStream_t stream) {
   if (a.max_chunks <= 1) return hipSuccess;  // every sequence is finished by the partial kernel
   dim3 grid(a.f.num_seqs * a.f.hkv);
-  if (fp32)
-    hipLaunchKernelGGL(decode_merge_kernel<float>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(decode_merge_kernel<bf16>, grid, dim3(256), 0, stream, a);
+  if (a.f.d == 128) {
+    if (fp32)
+      hipLaunchKernelGGL((decode_merge_kernel<float, 128>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_merge_kernel<bf16, 128>), grid, dim3(256), 0, stream, a);
+  } else {
+    if (fp32)
+      hipLaunchKernelGGL((decode_merge_kernel<float, 64>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_merge_kernel<bf16, 64>), grid, dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -42,17 +42,18 @@ namespace attn_sink {
 // cannot overflow for any realistic length and |v|.
 constexpr float kTileSumMax = 18446744073709551616.f;  // 2^64
 
-template <typename T>
+template <typename T, int D>
 struct FwdCfg {
   static constexpr int BM = 128;       // query rows per workgroup
   static constexpr int BN = 64;        // keys per tile
   static constexpr int THREADS = 256;  // 4 wavefronts x 32 rows
-  static constexpr int TILE = tile_elems<T>(BN);
+  static constexpr int TILE = tile_elems_d<T, D>(BN);
 };
 
-template <typename T>
+// D: head dim (64 or 128).
+template <typename T, int D>
 __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
-  using C = FwdCfg<T>;
+  using C = FwdCfg<T, D>;
   using M = Mfma<T>;
   using Frag = typename M::Frag;
   constexpr int E = M::E, KS = M::KS;
@@ -85,18 +86,18 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
   int wlo = p.window > 0 ? clampi(qw + off - p.window + 1, 0, nk) : 0;
   if (!wave_rows) whi = wlo = 0;
 
-  const size_t kv_row = (size_t)p.hkv * kD;
-  const T* kbase_p = static_cast<const T*>(p.k) + (size_t)sk.start * kv_row + g * kD;
-  const T* vbase_p = static_cast<const T*>(p.v) + (size_t)sk.start * kv_row + g * kD;
+  const size_t kv_row = (size_t)p.hkv * D;
+  const T* kbase_p = static_cast<const T*>(p.k) + (size_t)sk.start * kv_row + g * D;
+  const T* vbase_p = static_cast<const T*>(p.v) + (size_t)sk.start * kv_row + g * D;
 
   // Q fragments (B operand of S^T = K Q^T): lane owns query qw + c, d = KS*s + E*h + e.
   const int qi = qw + c;
-  typename M::Frag qf[kD / KS];
+  typename M::Frag qf[D / KS];
   {
     const bool ok = qi < nq;
-    const T* src = static_cast<const T*>(p.q) + ((size_t)(sq.start + (ok ? qi : 0)) * p.hq + head) * kD;
+    const T* src = static_cast<const T*>(p.q) + ((size_t)(sq.start + (ok ? qi : 0)) * p.hq + head) * D;
 #pragma unroll
-    for (int s = 0; s < kD / KS; ++s) qf[s] = global_frag<T>(src + KS * s + E * h, ok);
+    for (int s = 0; s < D / KS; ++s) qf[s] = global_frag<T>(src + KS * s + E * h, ok);
   }
 
   const float sink = p.sinks[head];
@@ -104,9 +105,9 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
   const float sl2 = p.scale * kLog2e;
   float m_run = sink2;  // running max in the exp2 domain, seeded with the sink logit
   float l_run = 0.f;    // this lane's partial sum of exp2(x - m_run) over its keys
-  f32x16 oacc[2];
+  f32x16 oacc[D / 32];  // O^T: [D x 32 rows]
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < D / 32; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[t][r] = 0.f;
 
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
   const Span row_keys = keys_of_row(qi, off, nk, p.causal, p.window);  // the keys row qi sees
   FragAddr<T> fa;
   fa.init(lane);
-  TileLoader<T, C::BN, C::THREADS> kld, vld;
+  TileLoaderD<T, C::BN, C::THREADS, D> kld, vld;
   kld.init(kbase_p, kv_row, nk, tid);
   vld.init(vbase_p, kv_row, nk, tid);
   if (kt_begin < kt_end) {
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[mt][r] = 0.f;
 #pragma unroll
-      for (int s = 0; s < kD / KS; ++s) st[mt] = M::mma(fa.row(Ks, mt, s), qf[s], st[mt]);
+      for (int s = 0; s < D / KS; ++s) st[mt] = M::mma(frag_row<T, C::BN>(fa, Ks, mt, s), qf[s], st[mt]);
     }
     if constexpr (!FULL) {
       // key of register r in tile mt: kbase + 4h + (32 mt + 8 (r/4) + r%4), a constant per element
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
       const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);  // 0 when m_run = -inf
       l_run *= alpha;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < D / 32; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
       m_run = m_new;
@@ -202,7 +203,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
 #pragma unroll
     for (int s = 0; s < NP; ++s)
 #pragma unroll
-      for (int md = 0; md < 2; ++md) oacc[md] = M::mma(fa.col(Vs, md, s), pf[s], oacc[md]);
+      for (int md = 0; md < D / 32; ++md) oacc[md] = M::mma(frag_col<T, C::BN>(fa, Vs, md, s), pf[s], oacc[md]);
   };
   // One pipeline step: start loading tile kt+1 into the other buffer, compute tile
   // kt, wait for the load, barrier.  `cur` / `nxt` are the two buffers (K then V).
@@ -265,9 +266,9 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
   if (sink2 > -INFINITY) l_tot += fast_exp2(sink2 - m_use);  // m_run >= sink2: at most 1
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qi < nq) {
-    T* dst = static_cast<T*>(p.o) + ((size_t)(sq.start + qi) * p.hq + head) * kD;
+    T* dst = static_cast<T*>(p.o) + ((size_t)(sq.start + qi) * p.hq + head) * D;
 #pragma unroll
-    for (int md = 0; md < 2; ++md)
+    for (int md = 0; md < D / 32; ++md)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d0 = 32 * md + crow(4 * r4, h);
@@ -287,13 +288,20 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int fp32, hipStream_t stream) {
-  const int tiles = (a.max_q + FwdCfg<bf16>::BM - 1) / FwdCfg<bf16>::BM;
+  const int tiles = (a.max_q + FwdCfg<bf16, 64>::BM - 1) / FwdCfg<bf16, 64>::BM;
   if (tiles == 0 || a.num_seqs == 0) return hipSuccess;
   dim3 grid(a.hq * a.num_seqs, tiles);
-  if (fp32)
-    hipLaunchKernelGGL(fwd_kernel<float>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(fwd_kernel<bf16>, grid, dim3(256), 0, stream, a);
+  if (a.d == 128) {
+    if (fp32)
+      hipLaunchKernelGGL((fwd_kernel<float, 128>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((fwd_kernel<bf16, 128>), grid, dim3(256), 0, stream, a);
+  } else {
+    if (fp32)
+      hipLaunchKernelGGL((fwd_kernel<float, 64>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((fwd_kernel<bf16, 64>), grid, dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

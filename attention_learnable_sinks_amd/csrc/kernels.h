@@ -6,7 +6,8 @@
 
 namespace attn_sink {
 
-constexpr int kHeadDimBuilt = 64;  // the only head dim the kernels are built for
+// Head dims the kernels are built for.
+inline bool head_dim_built(int d) { return d == 64 || d == 128; }
 
 struct FwdArgs {
   const void* q;
@@ -20,6 +21,7 @@ struct FwdArgs {
   int hq, hkv, num_seqs, total_q, total_k, max_q, max_k;
   float scale;
   int causal, window;
+  int d;  // head dim: 64 or 128
 };
 
 struct BwdArgs {
@@ -41,7 +43,7 @@ struct BwdArgs {
 // Forward for a few query rows per sequence against long key ranges, split over keys.
 struct DecodeArgs {
   FwdArgs f;
-  float* part_o;   // [num_seqs * hkv, max_chunks, cols, 64]: unnormalised O of each key chunk
+  float* part_o;   // [num_seqs * hkv, max_chunks, cols, d]: unnormalised O of each key chunk
   float* part_ml;  // [num_seqs * hkv, max_chunks, cols, 2]: (running max, sum) in the exp2 domain
   int chunk;       // key tiles (of 64) per chunk
   int max_chunks;  // chunks of the longest visible key range (grid y)
@@ -56,7 +58,7 @@ struct MergeArgs {
   const float* sinks;      // [hq]
   void* o;                 // [total_q, hq, 64]
   float* lse;              // [hq, total_q], sink included
-  int parts, hq, total_q;
+  int parts, hq, total_q, d;
 };
 
 // Kernel identifiers for the opt-in timing records.
@@ -71,14 +73,15 @@ struct BwdWorkspace {
   size_t rowstat, dsink_part, dk_part, dv_part, total;
   int pre_blocks, splits;
 };
-BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k, int num_seqs);
+BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k, int num_seqs, int d);
 int bwd_head_splits(int hq, int hkv, int total_k, int num_seqs);
 
 struct DecodeWorkspace {
   size_t part_o, part_ml, total;
   int chunk, max_chunks, cols, hw;
 };
-DecodeWorkspace decode_workspace_layout(int fp32, int hq, int hkv, int num_seqs, int max_q, int max_k, int window);
+DecodeWorkspace decode_workspace_layout(int fp32, int hq, int hkv, int num_seqs, int max_q, int max_k, int window,
+                                        int d);
 // The query heads of one kv head times the rows of one sequence fill at most 32 columns.
 bool decode_supported(int hq, int hkv, int max_q);
 

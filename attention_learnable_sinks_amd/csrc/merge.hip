@@ -16,17 +16,18 @@
 
 namespace attn_sink {
 
-// One wavefront per (row, head), lane = d; 4 per workgroup.
-template <typename T>
+// One wavefront per (row, head), lane = d (and d + 64 when D = 128); 4 per workgroup.
+template <typename T, int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  constexpr int DL = D / 64;  // values of d per lane
   const long long pair = (long long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const long long pairs = (long long)a.total_q * a.hq;
   if (pair >= pairs) return;
   const int row = (int)(pair / a.hq), head = (int)(pair % a.hq);
   const int d = threadIdx.x & 63;
   const size_t lse_at = (size_t)head * a.total_q + row;       // [part][Hq][total_q]
-  const size_t o_at = ((size_t)row * a.hq + head) * kD + d;   // [part][total_q][Hq][64]
-  const size_t lse_stride = (size_t)a.hq * a.total_q, o_stride = (size_t)a.total_q * a.hq * kD;
+  const size_t o_at = ((size_t)row * a.hq + head) * D + d;    // [part][total_q][Hq][D]
+  const size_t lse_stride = (size_t)a.hq * a.total_q, o_stride = (size_t)a.total_q * a.hq * D;
   const T* o_parts = static_cast<const T*>(a.o_parts);
   const float sink = a.sinks[head];
   constexpr int U = 8;
@@ -36,26 +37,32 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     for (int u = 0; u < U; ++u)
       if (s0 + u < a.parts) mm = fmaxf(mm, a.lse_parts[(size_t)(s0 + u) * lse_stride + lse_at]);
   }
-  float o = 0.f, l = 0.f;
+  float o[DL], l = 0.f;
+#pragma unroll
+  for (int j = 0; j < DL; ++j) o[j] = 0.f;
   if (mm > -INFINITY) {
     l = sink > -INFINITY ? __expf(sink - mm) : 0.f;  // the sink's mass, once
     for (int s0 = 0; s0 < a.parts; s0 += U) {
-      float ls[U], os[U];
+      float ls[U], os[U][DL];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const bool ok = s0 + u < a.parts;
         ls[u] = ok ? a.lse_parts[(size_t)(s0 + u) * lse_stride + lse_at] : -INFINITY;
-        os[u] = ok ? to_f32(o_parts[(size_t)(s0 + u) * o_stride + o_at]) : 0.f;
+#pragma unroll
+        for (int j = 0; j < DL; ++j) os[u][j] = ok ? to_f32(o_parts[(size_t)(s0 + u) * o_stride + o_at + 64 * j]) : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const float w = ls[u] == -INFINITY ? 0.f : __expf(ls[u] - mm);  // a shard the row does not see
         l += w;
-        o += w * os[u];
+#pragma unroll
+        for (int j = 0; j < DL; ++j) o[j] += w * os[u][j];
       }
     }
   }
-  static_cast<T*>(a.o)[((size_t)row * a.hq + head) * kD + d] = from_f32<T>(l > 0.f ? o / l : 0.f);
+#pragma unroll
+  for (int j = 0; j < DL; ++j)
+    static_cast<T*>(a.o)[((size_t)row * a.hq + head) * D + d + 64 * j] = from_f32<T>(l > 0.f ? o[j] / l : 0.f);
   if (d == 0) a.lse[lse_at] = l > 0.f ? mm + __logf(l) : -INFINITY;
 }
 
@@ -63,10 +70,17 @@ hipError_t launch_merge(const MergeArgs& a, int fp32, hipStream_t stream) {
   const long long pairs = (long long)a.total_q * a.hq;
   if (pairs == 0) return hipSuccess;
   dim3 grid((unsigned)((pairs + 3) / 4));
-  if (fp32)
-    hipLaunchKernelGGL(merge_kernel<float>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(merge_kernel<bf16>, grid, dim3(256), 0, stream, a);
+  if (a.d == 128) {
+    if (fp32)
+      hipLaunchKernelGGL((merge_kernel<float, 128>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((merge_kernel<bf16, 128>), grid, dim3(256), 0, stream, a);
+  } else {
+    if (fp32)
+      hipLaunchKernelGGL((merge_kernel<float, 64>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((merge_kernel<bf16, 64>), grid, dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

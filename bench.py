@@ -103,7 +103,8 @@ def cpu_baseline(inp: dict, workload, pairs: int, budget_s: float = 12.0, gpu_ou
                 errs[name] = max(errs.get(name, 0.0), e)
         if t_total >= budget_s:
             break
-    flop = pairs * group * done * 4 * 64 + pairs * group * done * 10 * 64
+    d = workload.head_dim
+    flop = pairs * group * done * 4 * d + pairs * group * done * 10 * d
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return dict(value=round(flop / t_total / 1e12, 6), unit="TFLOP/s", cores=int(threads), kind="oracle",
                 sample=f"{workload.name}: kv groups 0..{done - 1} ({done * group} of {workload.num_heads_q} query "
@@ -151,10 +152,11 @@ def decode_bench(als, torch, dev, steps: int, warmup: int) -> dict:
         keys = sum(min(n, window + rows - 1) if window > 0 else n for n in w.cache_lens)
         elem = 2 if w.dtype == "bf16" else 4
         tq = d["q"].shape[0]
-        byts = 2 * keys * w.num_heads_kv * 64 * elem + 2 * tq * w.num_heads_q * 64 * elem + tq * w.num_heads_q * 4
+        hd = w.head_dim
+        byts = 2 * keys * w.num_heads_kv * hd * elem + 2 * tq * w.num_heads_q * hd * elem + tq * w.num_heads_q * 4
         dec_ms = sum(timings["decode"][1].values())
         part_ms = timings["decode"][1].get("attn_sink_decode_partial_kernel", float("nan"))
-        kv_part = 2 * keys * w.num_heads_kv * 64 * elem + tq * w.num_heads_q * 64 * elem  # partial kernel: K, V, Q
+        kv_part = 2 * keys * w.num_heads_kv * hd * elem + tq * w.num_heads_q * hd * elem  # partial kernel: K, V, Q
         part_gbs = kv_part / (part_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(part_gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(part_gbs / PEAK_HBM_GBS, 4),
@@ -261,8 +263,9 @@ def main():
                 "steps": args.cold_steps}
 
     pairs = count_pairs(w.seqlens, causal, window)
-    fwd_flop = 4 * 64 * pairs * w.num_heads_q
-    bwd_flop = 10 * 64 * pairs * w.num_heads_q
+    hd = w.head_dim
+    fwd_flop = 4 * hd * pairs * w.num_heads_q
+    bwd_flop = 10 * hd * pairs * w.num_heads_q
     ms = (t1 - t0) * 1e3 / args.steps
     value = (fwd_flop + bwd_flop) / (ms * 1e-3) / 1e12
 
@@ -277,7 +280,7 @@ def main():
     t_tok, hq, hkv = w.total, w.num_heads_q, w.num_heads_kv
     mfma_peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     # Algorithmic bytes per launch (each operand moved once) and FLOP per launch.
-    qb, kb = t_tok * hq * 64 * elem, t_tok * hkv * 64 * elem  # one [T, Hq, 64] / [T, Hkv, 64] tensor
+    qb, kb = t_tok * hq * hd * elem, t_tok * hkv * hd * elem  # one [T, Hq, d] / [T, Hkv, d] tensor
     rows = t_tok * hq * 4                                       # one fp32 value per row and head
     kern_bytes = {
         "attn_sink_fwd_kernel": qb + 2 * kb + qb + rows,                 # Q, K, V -> O, LSE
@@ -288,7 +291,7 @@ def main():
     }
     gemm_d = {"attn_sink_fwd_kernel": 4, "attn_sink_bwd_dq_kernel": 6, "attn_sink_bwd_dkdv_kernel": 8}
     ridge = mfma_peak * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP per byte where the two peaks meet
-    flop = gemm_d.get(dom, 0) * 64 * pairs * hq
+    flop = gemm_d.get(dom, 0) * hd * pairs * hq
     byts = kern_bytes.get(dom, 0)
     if flop > 0 and flop / max(byts, 1) >= ridge:
         work, unit, bound, peak = flop / 1e12, "TFLOP/s", "mfma", mfma_peak

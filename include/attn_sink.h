@@ -63,7 +63,7 @@ extern "C" {
 typedef enum {
   ATTN_SINK_OK = 0,
   ATTN_SINK_ERR_INVALID_ARG = 1,  /* null pointer, bad count, Hq % Hkv != 0, ... */
-  ATTN_SINK_ERR_UNSUPPORTED = 2,  /* well-formed but not built: head_dim != 64, dtype, decode width */
+  ATTN_SINK_ERR_UNSUPPORTED = 2,  /* well-formed but not built: head_dim not 64 or 128, dtype, decode width */
   ATTN_SINK_ERR_WORKSPACE = 3,    /* workspace missing, misaligned or smaller than required */
   ATTN_SINK_ERR_HIP = 4           /* the HIP runtime refused a launch */
 } attn_sink_status;
@@ -75,7 +75,7 @@ typedef enum {
 
 typedef struct {
   int dtype;               /* attn_sink_dtype */
-  int head_dim;            /* must be 64 */
+  int head_dim;            /* 64 or 128 */
   int num_heads_q;         /* Hq  >= 1 */
   int num_heads_kv;        /* Hkv >= 1, Hq % Hkv == 0 (GQA: heads h of one kv head are contiguous) */
   int num_seqs;            /* >= 1 */

@@ -26,6 +26,21 @@ def _declared():
     return sorted(set(re.findall(r"\b(attn_sink_\w+)\s*\(", src)))
 
 
+def test_head_dim_128_is_accepted(lib):
+    """head_dim 64 and 128 are built: a d=128 shape passes every check (and stops at
+    the workspace check here), with workspaces sized for 128 columns."""
+    s = _shape(head_dim=128, num_heads_q=64, num_heads_kv=8, total_q=4096, total_k=4096, max_seqlen_q=4096,
+               max_seqlen_k=4096)
+    n128 = lib.attn_sink_bwd_workspace_bytes(ctypes.byref(s))
+    s64 = _shape(num_heads_q=64, num_heads_kv=8, total_q=4096, total_k=4096, max_seqlen_q=4096, max_seqlen_k=4096)
+    n64 = lib.attn_sink_bwd_workspace_bytes(ctypes.byref(s64))
+    assert n128 - n64 == 2 * 4 * 4096 * 8 * 64 * 4  # the dK/dV partials double (4 splits)
+    assert lib.attn_sink_bwd(ctypes.byref(s), *[FAKE] * 11, FAKE, n128 - 1, None) == als.ERR_WORKSPACE
+    d = _decode_shape(head_dim=128)
+    assert lib.attn_sink_fwd_decode_workspace_bytes(ctypes.byref(d)) > 0
+    assert lib.attn_sink_merge(als.BF16, 128, 8, 0, 2, None, None, FAKE, None, None, None) == als.OK
+
+
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["attn_sink_fwd", "attn_sink_bwd", "attn_sink_bwd_workspace_bytes",
                                   "attn_sink_fwd_decode", "attn_sink_fwd_decode_workspace_bytes", "attn_sink_merge",
@@ -56,7 +71,8 @@ def _shape(**kw):
 
 
 BAD_SHAPES = [
-    (dict(head_dim=128), als.ERR_UNSUPPORTED),
+    (dict(head_dim=96), als.ERR_UNSUPPORTED),
+    (dict(head_dim=256), als.ERR_UNSUPPORTED),
     (dict(head_dim=0), als.ERR_INVALID_ARG),
     (dict(dtype=7), als.ERR_UNSUPPORTED),
     (dict(num_heads_q=6, num_heads_kv=4), als.ERR_INVALID_ARG),
@@ -158,7 +174,7 @@ def test_fwd_decode_workspace(lib):
 
 
 @pytest.mark.parametrize("args,status", [
-    ((als.BF16, 128, 8, 10, 2), als.ERR_UNSUPPORTED),
+    ((als.BF16, 96, 8, 10, 2), als.ERR_UNSUPPORTED),
     ((7, 64, 8, 10, 2), als.ERR_UNSUPPORTED),
     ((als.BF16, 0, 8, 10, 2), als.ERR_INVALID_ARG),
     ((als.BF16, 64, 0, 10, 2), als.ERR_INVALID_ARG),

@@ -59,6 +59,9 @@ WORKLOADS = {
                        ((True, 0, ("normal",)), (True, 128, ("normal",)))),
     "long_20k": Workload("long_20k", (20480,), 64, 8, 64, "bf16", 4,
                          ((True, 0, ("uniform", -2.0, 8.0)),)),
+    # head dim 128 at the same width (32 query heads x 128 = 64 x 64), 4k causal
+    "d128_4k": Workload("d128_4k", (4096,), 32, 8, 128, "bf16", 7, ((True, 0, ("normal",)),),
+                        softmax_scale=128 ** -0.5),
 }
 
 
