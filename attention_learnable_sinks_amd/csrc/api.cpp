@@ -177,7 +177,8 @@ attn_sink_status attn_sink_fwd_decode(const attn_sink_shape* shape, const void* 
 
 size_t attn_sink_bwd_workspace_bytes(const attn_sink_shape* shape) {
   if (check_shape(shape) != ATTN_SINK_OK) return 0;
-  return bwd_workspace_layout(shape->num_heads_q, shape->num_heads_kv, shape->total_q, shape->total_k, shape->num_seqs, shape->head_dim).total;
+  return bwd_workspace_layout(shape->num_heads_q, shape->num_heads_kv, shape->total_q, shape->total_k, shape->num_seqs,
+                              shape->causal, shape->window > 0 ? shape->window : 0, shape->head_dim).total;
 }
 
 attn_sink_status attn_sink_bwd(const attn_sink_shape* shape, const void* q, const void* k, const void* v,
@@ -190,7 +191,8 @@ attn_sink_status attn_sink_bwd(const attn_sink_shape* shape, const void* q, cons
   if (!sinks || !dsinks) return ATTN_SINK_ERR_INVALID_ARG;
   if (any_q && (!q || !o || !lse || !dout || !dq)) return ATTN_SINK_ERR_INVALID_ARG;
   if (any_k && (!k || !v || !dk || !dv)) return ATTN_SINK_ERR_INVALID_ARG;
-  const BwdWorkspace ws = bwd_workspace_layout(shape->num_heads_q, shape->num_heads_kv, shape->total_q, shape->total_k, shape->num_seqs, shape->head_dim);
+  const BwdWorkspace ws = bwd_workspace_layout(shape->num_heads_q, shape->num_heads_kv, shape->total_q, shape->total_k, shape->num_seqs,
+                              shape->causal, shape->window > 0 ? shape->window : 0, shape->head_dim);
   if (!workspace || workspace_bytes < ws.total || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
     return ATTN_SINK_ERR_WORKSPACE;
 

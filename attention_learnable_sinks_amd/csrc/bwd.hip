@@ -578,35 +578,50 @@ __global__ __launch_bounds__(256) void bwd_finish_kernel(BwdArgs a) {
 // ----------------------------------------------------------------------------- launchers
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int bwd_head_splits(int hq, int hkv, int total_k, int num_seqs) {
+int bwd_head_splits(int hq, int hkv, int total_k, int num_seqs, int causal, int window, int d) {
   // The dK/dV grid has one workgroup per (sequence, kv head, head split, folded pair
-  // of 128-key tiles), all of about the same work for one sequence length, and
-  // about 512 of them run at once (256 CUs x 2).  Splitting the query heads of a
-  // kv head over s workgroups divides the work per workgroup by s, so the time
-  // goes as ceil(workgroups / 512) / s: pick the s that minimises it (the fewest
-  // splits on a tie, as every split adds float32 partials to reduce).
+  // of 128-key tiles); about 512 of them run at once (256 CUs x 2).  Splitting the
+  // query heads of a kv head over s workgroups divides each workgroup's work by s
+  // but multiplies the grid by s and adds float32 partials (written here, read back
+  // by the finish kernel).  Estimated time, in microseconds:
+  //   rounds(s) x (group / s) x steps x 2.25  +  partial bytes(s) / 5 TB/s
+  // where steps is the number of (query head, 64-row tile) steps one folded pair
+  // takes for one head (from the mean sequence length, the mask and the window) and
+  // 2.25 us is the measured time of one step with two workgroups per compute unit.
+  // Pick the cheapest s (the fewest splits on a tie).
   const int group = hq / hkv;
   long long pairs = (total_k + 255) / 256 + num_seqs / 2;  // folded pairs over all sequences (approx.)
   if (pairs < 1) pairs = 1;
+  const long long n = num_seqs > 0 ? (long long)total_k / num_seqs : total_k;  // mean sequence length
+  long long steps;
+  if (window > 0) {
+    const long long w = window < n ? window : n;
+    steps = 2 * ((w + 128 + 63) / 64 + 1);  // each tile of the pair sees about window + 128 rows
+  } else {
+    steps = causal ? n / 64 + 2 : 2 * (n / 64 + 1);
+  }
+  if (steps < 1) steps = 1;
   constexpr long long kConcurrent = 512;
+  const double part_bytes = 2.0 * 2.0 * (double)total_k * hkv * d * 4.0;  // dK + dV, written and read, per split
   int best = 1;
-  long long best_num = 0, best_den = 1;  // cost = rounds / s as a fraction
+  double best_t = 0.0;
   for (int sp = 1; sp <= group && group % sp == 0; sp *= 2) {
     const long long rounds = (pairs * hkv * sp + kConcurrent - 1) / kConcurrent;
-    if (sp == 1 || rounds * best_den < best_num * sp) {
+    const double t = (double)rounds * (double)(group / sp) * (double)steps * 2.25 + (sp > 1 ? sp * part_bytes / 5e6 : 0.0);
+    if (sp == 1 || t < best_t) {
       best = sp;
-      best_num = rounds;
-      best_den = sp;
+      best_t = t;
     }
   }
   return best;
 }
 
-BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k, int num_seqs, int d) {
+BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k, int num_seqs, int causal, int window,
+                                  int d) {
   BwdWorkspace w;
   const int rows = total_q > 0 ? total_q : 1;
   w.pre_blocks = (rows + kPreRows - 1) / kPreRows;
-  w.splits = bwd_head_splits(hq, hkv, total_k, num_seqs);
+  w.splits = bwd_head_splits(hq, hkv, total_k, num_seqs, causal, window, d);
   size_t o = 0;
   w.rowstat = o;     o = align256(o + (size_t)hq * 2 * total_q * 4);
   w.dsink_part = o;  o = align256(o + (size_t)hq * w.pre_blocks * 4);

@@ -73,8 +73,9 @@ struct BwdWorkspace {
   size_t rowstat, dsink_part, dk_part, dv_part, total;
   int pre_blocks, splits;
 };
-BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k, int num_seqs, int d);
-int bwd_head_splits(int hq, int hkv, int total_k, int num_seqs);
+BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k, int num_seqs, int causal, int window,
+                                  int d);
+int bwd_head_splits(int hq, int hkv, int total_k, int num_seqs, int causal, int window, int d);
 
 struct DecodeWorkspace {
   size_t part_o, part_ml, total;
