@@ -16,7 +16,6 @@ namespace attn_sink {
 const char* kernel_name(int id) {
   switch (id) {
     case K_FWD: return "attn_sink_fwd_kernel";
-    case K_BWD_PRE: return "attn_sink_bwd_pre_kernel";
     case K_BWD_DQ: return "attn_sink_bwd_dq_kernel";
     case K_BWD_DKDV: return "attn_sink_bwd_dkdv_kernel";
     case K_BWD_FINISH: return "attn_sink_bwd_finish_kernel";
@@ -178,7 +177,8 @@ attn_sink_status attn_sink_fwd_decode(const attn_sink_shape* shape, const void* 
 size_t attn_sink_bwd_workspace_bytes(const attn_sink_shape* shape) {
   if (check_shape(shape) != ATTN_SINK_OK) return 0;
   return bwd_workspace_layout(shape->num_heads_q, shape->num_heads_kv, shape->total_q, shape->total_k, shape->num_seqs,
-                              shape->causal, shape->window > 0 ? shape->window : 0, shape->head_dim).total;
+                              shape->max_seqlen_q, shape->causal, shape->window > 0 ? shape->window : 0,
+                              shape->head_dim).total;
 }
 
 attn_sink_status attn_sink_bwd(const attn_sink_shape* shape, const void* q, const void* k, const void* v,
@@ -192,7 +192,8 @@ attn_sink_status attn_sink_bwd(const attn_sink_shape* shape, const void* q, cons
   if (any_q && (!q || !o || !lse || !dout || !dq)) return ATTN_SINK_ERR_INVALID_ARG;
   if (any_k && (!k || !v || !dk || !dv)) return ATTN_SINK_ERR_INVALID_ARG;
   const BwdWorkspace ws = bwd_workspace_layout(shape->num_heads_q, shape->num_heads_kv, shape->total_q, shape->total_k, shape->num_seqs,
-                              shape->causal, shape->window > 0 ? shape->window : 0, shape->head_dim);
+                              shape->max_seqlen_q, shape->causal, shape->window > 0 ? shape->window : 0,
+                              shape->head_dim);
   if (!workspace || workspace_bytes < ws.total || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
     return ATTN_SINK_ERR_WORKSPACE;
 
@@ -212,12 +213,10 @@ attn_sink_status attn_sink_bwd(const attn_sink_shape* shape, const void* q, cons
   a.splits = ws.splits;
   const int fp32 = shape->dtype == ATTN_SINK_FP32;
 
-  st = timed_launch(K_BWD_PRE, stream, [&] { return launch_bwd_pre(a, fp32, stream); });
+  // The dQ kernel also writes the row statistics and the dS_h partials, so it runs
+  // even without query rows (its workgroups then only write zero partials).
+  st = timed_launch(K_BWD_DQ, stream, [&] { return launch_bwd_dq(a, fp32, stream); });
   if (st != ATTN_SINK_OK) return st;
-  if (any_q) {
-    st = timed_launch(K_BWD_DQ, stream, [&] { return launch_bwd_dq(a, fp32, stream); });
-    if (st != ATTN_SINK_OK) return st;
-  }
   if (any_k) {
     st = timed_launch(K_BWD_DKDV, stream, [&] { return launch_bwd_dkdv(a, fp32, stream); });
     if (st != ATTN_SINK_OK) return st;

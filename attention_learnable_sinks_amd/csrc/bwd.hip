@@ -11,14 +11,16 @@
 // P is recomputed from the forward's lse (which includes the sink), so the sink
 // needs no other state in the backward.
 //
-// Four kernels on one stream, none using atomics, so every output is bitwise
+// Three kernels on one stream, none using atomics, so every output is bitwise
 // reproducible:
-//   1. bwd_pre:    D_i and per-block partial sums of -P_sink_i D_i.
-//   2. bwd_dq:     query-stationary (like the forward): per 64-key tile,
-//                  S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T, with Q and dO in
-//                  registers and K^T read from the row-major K tile by transposing
-//                  LDS loads.  dQ is written once, scaled, in the element type.
-//   3. bwd_dkdv:   key-stationary: a workgroup owns 128 keys of one kv head (32 per
+//   1. bwd_dq:     query-stationary (like the forward): D_i = <dO_i, O_i> from the
+//                  row's own O and dO fragments, the row statistics (lse * log2 e,
+//                  -D) for the dK/dV kernel and a per-workgroup partial sum of
+//                  -P_sink_i D_i; then per 64-key tile S^T = K Q^T, dP^T = V dO^T,
+//                  dQ^T += K^T dS^T, with Q and dO in registers and K^T read from
+//                  the row-major K tile by transposing LDS loads.  dQ is written
+//                  once, scaled, in the element type.
+//   2. bwd_dkdv:   key-stationary: a workgroup owns 128 keys of one kv head (32 per
 //                  wavefront, K and V in registers) and loops over the query heads of
 //                  its share of the GQA group and over the query tiles of the band:
 //                  S = Q K^T, dP = dO V^T put the key on the lane, so P and dS feed
@@ -27,7 +29,7 @@
 //                  tiles kt and n-1-kt are folded into one workgroup so all workgroups
 //                  carry the same work.  When the group is split over several
 //                  workgroups (to fill the GPU), each split writes an fp32 partial.
-//   4. bwd_finish: fixed-order sums of the dS_h partials and of the dK/dV partials.
+//   3. bwd_finish: fixed-order sums of the dS_h partials and of the dK/dV partials.
 #include <type_traits>
 #include <utility>
 
@@ -36,45 +38,7 @@
 
 namespace attn_sink {
 
-constexpr int kPreRows = 64;  // rows per bwd_pre workgroup
-
-// ----------------------------------------------------------------------------- 1. preprocess
-template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
-  const FwdArgs& f = a.f;
-  const int head = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int row = blockIdx.x * kPreRows + tid / 4;
-  const int part = tid % 4;  // a quarter of the D columns
-  float contrib = 0.f;
-  if (row < f.total_q) {
-    const size_t base = ((size_t)row * f.hq + head) * D + part * (D / 4);
-    const T* o = static_cast<const T*>(f.o) + base;
-    const T* d = static_cast<const T*>(a.dout) + base;
-    float acc = 0.f;
-#pragma unroll
-    for (int e = 0; e < D / 4; ++e) acc += to_f32(o[e]) * to_f32(d[e]);
-    acc += __shfl_xor(acc, 1);
-    acc += __shfl_xor(acc, 2);
-    if (part == 0) {
-      const float lse = f.lse[(size_t)head * f.total_q + row];
-      a.rowstat[(size_t)(2 * head) * f.total_q + row] = lse * kLog2e;
-      a.rowstat[(size_t)(2 * head + 1) * f.total_q + row] = -acc;
-      const float sink = f.sinks[head];
-      const float ps = (lse > -INFINITY && sink > -INFINITY) ? fast_exp2((sink - lse) * kLog2e) : 0.f;
-      contrib = -ps * acc;
-    }
-  }
-  // Fixed-order block reduction of the sink-gradient contributions.
-  __shared__ float red[4];
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) contrib += __shfl_xor(contrib, m);
-  if ((tid & 63) == 0) red[tid >> 6] = contrib;
-  __syncthreads();
-  if (tid == 0) a.dsink_part[(size_t)head * a.pre_blocks + blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
-}
-
-// ----------------------------------------------------------------------------- 2. dQ
+// ----------------------------------------------------------------------------- 1. dQ
 template <typename T, int D>
 struct DqCfg {
   static constexpr int BM = 128;  // query rows per workgroup (4 wavefronts x 32)
@@ -90,6 +54,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   constexpr int E = M::E, KS = M::KS;
   const FwdArgs& f = a.f;
   __shared__ __attribute__((aligned(16))) T smem[4 * C::TILE];  // [buf][K, V]
+  __shared__ float red[4];
 
   const XcdSlot slot = xcd_slot(blockIdx.x, f.hkv, f.hq / f.hkv);
   const int b = slot.seq, g = slot.kv;
@@ -99,7 +64,12 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const SeqBounds sk = seq_bounds(f.cu_k, b, f.total_k);
   const int nq = sq.len, nk = sk.len, off = nk - nq;
   const int qs = tile * C::BM;
-  if (qs >= nq) return;
+  // This workgroup's slot of the dS_h partials (one per head, sequence and row tile).
+  float* const dsink_slot = a.dsink_part + (size_t)head * a.pre_blocks + (size_t)b * gridDim.y + tile;
+  if (qs >= nq) {
+    if (threadIdx.x == 0) *dsink_slot = 0.f;
+    return;
+  }
   const int qe = min(qs + C::BM, nq);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -124,23 +94,22 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const bool qok = qi < nq;
   Span row_keys = keys_of_row(qi, off, nk, f.causal, f.window);  // the keys row qi sees
   if (!qok) row_keys.len = 0u;
-  typename M::Frag qf[D / KS], dof[D / KS];
+  // Q, dO and O fragments of the lane's row (lane half h holds half of it); O only
+  // for D_i = <dO_i, O_i>.
+  typename M::Frag qf[D / KS], dof[D / KS], of[D / KS];
   {
     const size_t o = ((size_t)(sq.start + (qok ? qi : 0)) * f.hq + head) * D;
     const T* qsrc = static_cast<const T*>(f.q) + o;
     const T* dsrc = static_cast<const T*>(a.dout) + o;
+    const T* osrc = static_cast<const T*>(f.o) + o;
 #pragma unroll
     for (int s = 0; s < D / KS; ++s) {
       qf[s] = global_frag<T>(qsrc + KS * s + E * h, qok);
       dof[s] = global_frag<T>(dsrc + KS * s + E * h, qok);
+      of[s] = global_frag<T>(osrc + KS * s + E * h, qok);
     }
   }
-  const float lse2 = qok ? a.rowstat[(size_t)(2 * head) * f.total_q + sq.start + qi] : 0.f;
-  const float dd = qok ? -a.rowstat[(size_t)(2 * head + 1) * f.total_q + sq.start + qi] : 0.f;
-  const float sl2 = f.scale * kLog2e;
-  f32x16 neg_dd;  // -D of the lane's row in every register
-#pragma unroll
-  for (int r = 0; r < 16; ++r) neg_dd[r] = -dd;
+  const float lse = qok ? f.lse[(size_t)head * f.total_q + sq.start + qi] : 0.f;
 
   f32x16 dqt[D / 32];  // dQ^T [D x 32 q]
 #pragma unroll
@@ -148,6 +117,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqt[t][r] = 0.f;
 
+  // The first K/V tile is in flight while the row statistics are formed.
   const int kt_begin = klo / C::BN;
   const int kt_end = khi > klo ? (khi + C::BN - 1) / C::BN : kt_begin;
   TileLoaderD<T, C::BN, C::THREADS, D> kld, vld;
@@ -159,8 +129,33 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     kld.finish();
     vld.finish();
   }
+  float dpart = 0.f;
+#pragma unroll
+  for (int s = 0; s < D / KS; ++s) dpart = frag_dot<T>(of[s], dof[s], dpart);
+  const float dd = halves_sum(dpart);  // D of the lane's row (0 past the sequence)
+  const float lse2 = lse * kLog2e;
+  const float sl2 = f.scale * kLog2e;
+  // Row statistics for the dK/dV kernel, and this workgroup's share of
+  // dS_h = -sum_i P_sink_i D_i (fixed-order reduction: lanes, then wavefronts).
+  {
+    const bool writer = qok && h == 0;
+    if (writer) {
+      a.rowstat[(size_t)(2 * head) * f.total_q + sq.start + qi] = lse2;
+      a.rowstat[(size_t)(2 * head + 1) * f.total_q + sq.start + qi] = -dd;
+    }
+    const float sink = f.sinks[head];
+    const float ps = (writer && lse > -INFINITY && sink > -INFINITY) ? fast_exp2((sink - lse) * kLog2e) : 0.f;
+    float contrib = -ps * dd;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) contrib += __shfl_xor(contrib, m);
+    if (lane == 0) red[w] = contrib;
+  }
+  f32x16 neg_dd;  // -D of the lane's row in every register
+#pragma unroll
+  for (int r = 0; r < 16; ++r) neg_dd[r] = -dd;
   vmem_drain();
   __syncthreads();
+  if (tid == 0) *dsink_slot = (red[0] + red[1]) + (red[2] + red[3]);
 
   // One tile: S^T, dP^T, P^T, dS^T, dQ^T += K^T dS^T; FULL tiles need no mask.
   auto body = [&](const T* Ks, const T* Vs, int kbase, auto full_tag) {
@@ -263,7 +258,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
-// ----------------------------------------------------------------------------- 3. dK, dV
+// ----------------------------------------------------------------------------- 2. dK, dV
 template <typename T, int D>
 struct DkvCfg {
   static constexpr int BMB = 64;   // queries per tile
@@ -537,7 +532,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && D == 64) ? 2 : 1) void bwd_
   }
 }
 
-// ----------------------------------------------------------------------------- 4. finish
+// ----------------------------------------------------------------------------- 3. finish
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_finish_kernel(BwdArgs a) {
   const int D = a.f.d;
@@ -616,11 +611,11 @@ int bwd_head_splits(int hq, int hkv, int total_k, int num_seqs, int causal, int 
   return best;
 }
 
-BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k, int num_seqs, int causal, int window,
-                                  int d) {
+BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k, int num_seqs, int max_q, int causal,
+                                  int window, int d) {
   BwdWorkspace w;
-  const int rows = total_q > 0 ? total_q : 1;
-  w.pre_blocks = (rows + kPreRows - 1) / kPreRows;
+  // one dS_h partial per (head, sequence, dQ row tile): the dQ workgroups write them
+  w.pre_blocks = num_seqs * ((max_q + DqCfg<bf16, 64>::BM - 1) / DqCfg<bf16, 64>::BM);
   w.splits = bwd_head_splits(hq, hkv, total_k, num_seqs, causal, window, d);
   size_t o = 0;
   w.rowstat = o;     o = align256(o + (size_t)hq * 2 * total_q * 4);
@@ -630,22 +625,6 @@ BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k, int
   w.dv_part = o;     o = align256(o + part);
   w.total = o;
   return w;
-}
-
-hipError_t launch_bwd_pre(const BwdArgs& a, int fp32, hipStream_t stream) {
-  dim3 grid(a.pre_blocks, a.f.hq);
-  if (a.f.d == 128) {
-    if (fp32)
-      hipLaunchKernelGGL((bwd_pre_kernel<float, 128>), grid, dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL((bwd_pre_kernel<bf16, 128>), grid, dim3(256), 0, stream, a);
-  } else {
-    if (fp32)
-      hipLaunchKernelGGL((bwd_pre_kernel<float, 64>), grid, dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL((bwd_pre_kernel<bf16, 64>), grid, dim3(256), 0, stream, a);
-  }
-  return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, int fp32, hipStream_t stream) {

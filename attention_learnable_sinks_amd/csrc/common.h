@@ -281,6 +281,18 @@ __device__ inline float frag_sum(typename Mfma<T>::Frag f, float acc) {
   }
 }
 
+// acc + the dot product of two operand fragments (bf16: four v_dot2).
+template <typename T>
+__device__ inline float frag_dot(typename Mfma<T>::Frag a, typename Mfma<T>::Frag b, float acc) {
+  if constexpr (Mfma<T>::E == 8) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{a[e], a[e + 1]}, bf16x2{b[e], b[e + 1]}, acc, false);
+    return acc;
+  } else {
+    return fmaf(a, b, acc);
+  }
+}
+
 // ---------------------------------------------------------------- global <-> LDS staging
 // A tile of `ROWS` rows x 64 columns of one head, moved as 16-byte chunks (CPR per
 // row) with raw buffer loads: the buffer descriptor covers exactly the sequence's

@@ -32,8 +32,8 @@ struct BwdArgs {
   void* dv;
   float* dsinks;
   // workspace carve-up (float32, device)
-  float* rowstat;     // [hq, 2, total_q]: lse_i * log2(e), then -D_i with D_i = <dO_i, O_i>
-  float* dsink_part;  // [hq, pre_blocks]
+  float* rowstat;     // [hq, 2, total_q]: lse_i * log2(e), then -D_i with D_i = <dO_i, O_i> (written by bwd_dq)
+  float* dsink_part;  // [hq, pre_blocks]: per (sequence, dQ row tile) partial sums of -P_sink_i D_i
   float* dk_part;     // [splits, total_k, hkv, 64] (only when splits > 1)
   float* dv_part;     // [splits, total_k, hkv, 64] (only when splits > 1)
   int pre_blocks;
@@ -63,8 +63,8 @@ struct MergeArgs {
 
 // Kernel identifiers for the opt-in timing records.
 enum KernelId {
-  K_FWD = 0, K_BWD_PRE = 1, K_BWD_DQ = 2, K_BWD_DKDV = 3, K_BWD_FINISH = 4,
-  K_DEC_PARTIAL = 5, K_DEC_MERGE = 6, K_MERGE = 7, K_COUNT = 8
+  K_FWD = 0, K_BWD_DQ = 1, K_BWD_DKDV = 2, K_BWD_FINISH = 3,
+  K_DEC_PARTIAL = 4, K_DEC_MERGE = 5, K_MERGE = 6, K_COUNT = 7
 };
 const char* kernel_name(int id);
 
@@ -73,8 +73,8 @@ struct BwdWorkspace {
   size_t rowstat, dsink_part, dk_part, dv_part, total;
   int pre_blocks, splits;
 };
-BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k, int num_seqs, int causal, int window,
-                                  int d);
+BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k, int num_seqs, int max_q, int causal,
+                                  int window, int d);
 int bwd_head_splits(int hq, int hkv, int total_k, int num_seqs, int causal, int window, int d);
 
 struct DecodeWorkspace {
@@ -88,7 +88,6 @@ bool decode_supported(int hq, int hkv, int max_q);
 
 // Each launcher enqueues one kernel on `stream` and returns hipGetLastError().
 hipError_t launch_fwd(const FwdArgs& a, int fp32, hipStream_t stream);
-hipError_t launch_bwd_pre(const BwdArgs& a, int fp32, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int fp32, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int fp32, hipStream_t stream);
 hipError_t launch_bwd_finish(const BwdArgs& a, int fp32, hipStream_t stream);

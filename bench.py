@@ -284,8 +284,7 @@ def main():
     rows = t_tok * hq * 4                                       # one fp32 value per row and head
     kern_bytes = {
         "attn_sink_fwd_kernel": qb + 2 * kb + qb + rows,                 # Q, K, V -> O, LSE
-        "attn_sink_bwd_pre_kernel": 2 * qb + rows + 2 * rows,            # O, dO, LSE -> lse*log2e, -D
-        "attn_sink_bwd_dq_kernel": 2 * qb + 2 * kb + 2 * rows + qb,      # Q, dO, K, V, rows -> dQ
+        "attn_sink_bwd_dq_kernel": 3 * qb + 2 * kb + rows + qb + 2 * rows,  # Q, O, dO, K, V, LSE -> dQ, lse*log2e, -D
         "attn_sink_bwd_dkdv_kernel": 2 * qb + 2 * kb + 2 * rows + 2 * kb,  # Q, dO, K, V, rows -> dK, dV
         "attn_sink_bwd_finish_kernel": 2 * kb,
     }

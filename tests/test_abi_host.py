@@ -223,12 +223,13 @@ def test_workspace_size_formula(lib):
     n = lib.attn_sink_bwd_workspace_bytes(ctypes.byref(s))
     t, hq, hkv, d = 4096, 64, 8, 64
     splits = 4  # 16 folded key-tile pairs x 8 kv heads x 4 = 512 dK/dV workgroups
-    expect = hq * 2 * t * 4 + hq * (t // 64) * 4 + 2 * splits * t * hkv * d * 4
+    # row statistics, one dS_h partial per (head, sequence, 128-row dQ tile), dK/dV partials
+    expect = hq * 2 * t * 4 + hq * (t // 128) * 4 + 2 * splits * t * hkv * d * 4
     assert expect <= n <= expect + 4 * 256
     s = _shape(num_heads_q=64, num_heads_kv=8, total_q=16384, total_k=16384, max_seqlen_q=16384,
                max_seqlen_k=16384)
     n = lib.attn_sink_bwd_workspace_bytes(ctypes.byref(s))
-    expect = hq * 2 * 16384 * 4 + hq * (16384 // 64) * 4  # 64 pairs x 8 = 512: no split, no partials
+    expect = hq * 2 * 16384 * 4 + hq * (16384 // 128) * 4  # 64 pairs x 8 = 512: no split, no partials
     assert expect <= n <= expect + 4 * 256
 
 
