@@ -82,11 +82,16 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) T smem[kDecWaves * STAGES * 2 * TILE];
 
   const FwdArgs& f = a.f;
+  // Workgroups are dealt to the 8 XCDs by linear index (x + X y) mod 8.  Rotating the
+  // (sequence, kv-head block) column by the chunk row spreads each sequence's chunks
+  // over consecutive XCDs; without it a column (and so a whole sequence) stays on one
+  // XCD, and with ragged lengths the XCD holding the longest ones finishes last.
+  const int col = (int)((blockIdx.x + blockIdx.y) % gridDim.x);
   const int gblocks = f.hkv / a.hw;
-  const int b = blockIdx.x / gblocks;
+  const int b = col / gblocks;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = (blockIdx.x % gblocks) * a.hw + w;  // this wavefront's kv head
+  const int g = (col % gblocks) * a.hw + w;  // this wavefront's kv head
   const int h = lane >> 5, c = lane & 31;
   const int G = f.hq / f.hkv;
 
