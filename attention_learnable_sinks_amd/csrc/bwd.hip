@@ -261,14 +261,17 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 // ----------------------------------------------------------------------------- 2. dK, dV
 template <typename T, int D>
 struct DkvCfg {
-  static constexpr int BMB = 64;   // queries per tile
-  static constexpr int BNB = 128;  // keys per key tile (4 wavefronts x 32)
-  static constexpr int THREADS = 256;
+  static constexpr int BMB = 64;       // queries per tile
+  static constexpr int THREADS = 256;  // 4 wavefronts
+  static constexpr int BNB = 128;      // keys per key tile (32 per wavefront)
   static constexpr int TILE = tile_elems_d<T, D>(BMB);
+  // workgroups resident per compute unit (bf16 at d = 64 fits two; the others one)
+  static constexpr int PER_CU = (sizeof(T) == 2 && D == 64) ? 2 : 1;
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, (sizeof(T) == 2 && D == 64) ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__((DkvCfg<T, D>::THREADS), (sizeof(T) == 2 && D == 64) ? 2 : 1) void bwd_dkdv_kernel(
+    BwdArgs a) {
   using C = DkvCfg<T, D>;
   using M = Mfma<T>;
   constexpr int E = M::E, KS = M::KS;
@@ -573,30 +576,32 @@ __global__ __launch_bounds__(256) void bwd_finish_kernel(BwdArgs a) {
 // ----------------------------------------------------------------------------- launchers
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int bwd_head_splits(int hq, int hkv, int total_k, int num_seqs, int causal, int window, int d) {
+int bwd_head_splits(int hq, int hkv, int total_k, int num_seqs, int causal, int window, int d, int fp32) {
   // The dK/dV grid has one workgroup per (sequence, kv head, head split, folded pair
-  // of 128-key tiles); about 512 of them run at once (256 CUs x 2).  Splitting the
+  // of 128-key tiles); 256 or 512 run at once (one or two per compute unit, by the
+  // variant's registers).  Splitting the
   // query heads of a kv head over s workgroups divides each workgroup's work by s
   // but multiplies the grid by s and adds float32 partials (written here, read back
   // by the finish kernel).  Estimated time, in microseconds:
   //   rounds(s) x (group / s) x steps x 2.25  +  partial bytes(s) / 5 TB/s
   // where steps is the number of (query head, 64-row tile) steps one folded pair
   // takes for one head (from the mean sequence length, the mask and the window) and
-  // 2.25 us is the measured time of one step with two workgroups per compute unit.
-  // Pick the cheapest s (the fewest splits on a tie).
+  // 2.25 us is the measured time of one such step.  Pick the cheapest s (the fewest
+  // splits on a tie).
   const int group = hq / hkv;
-  long long pairs = (total_k + 255) / 256 + num_seqs / 2;  // folded pairs over all sequences (approx.)
+  const long long bnb = DkvCfg<bf16, 64>::BNB;  // keys per tile
+  long long pairs = (total_k + 2 * bnb - 1) / (2 * bnb) + num_seqs / 2;  // folded pairs (approx.)
   if (pairs < 1) pairs = 1;
   const long long n = num_seqs > 0 ? (long long)total_k / num_seqs : total_k;  // mean sequence length
   long long steps;
   if (window > 0) {
     const long long w = window < n ? window : n;
-    steps = 2 * ((w + 128 + 63) / 64 + 1);  // each tile of the pair sees about window + 128 rows
+    steps = 2 * ((w + bnb + 63) / 64 + 1);  // each tile of the pair sees about window + bnb rows
   } else {
-    steps = causal ? n / 64 + 2 : 2 * (n / 64 + 1);
+    steps = causal ? n / 64 + bnb / 64 : 2 * (n / 64 + 1);
   }
   if (steps < 1) steps = 1;
-  constexpr long long kConcurrent = 512;
+  const long long kConcurrent = 256LL * ((!fp32 && d == 64) ? DkvCfg<bf16, 64>::PER_CU : DkvCfg<float, 64>::PER_CU);
   const double part_bytes = 2.0 * 2.0 * (double)total_k * hkv * d * 4.0;  // dK + dV, written and read, per split
   int best = 1;
   double best_t = 0.0;
@@ -612,11 +617,11 @@ int bwd_head_splits(int hq, int hkv, int total_k, int num_seqs, int causal, int 
 }
 
 BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k, int num_seqs, int max_q, int causal,
-                                  int window, int d) {
+                                  int window, int d, int fp32) {
   BwdWorkspace w;
   // one dS_h partial per (head, sequence, dQ row tile): the dQ workgroups write them
   w.pre_blocks = num_seqs * ((max_q + DqCfg<bf16, 64>::BM - 1) / DqCfg<bf16, 64>::BM);
-  w.splits = bwd_head_splits(hq, hkv, total_k, num_seqs, causal, window, d);
+  w.splits = bwd_head_splits(hq, hkv, total_k, num_seqs, causal, window, d, fp32);
   size_t o = 0;
   w.rowstat = o;     o = align256(o + (size_t)hq * 2 * total_q * 4);
   w.dsink_part = o;  o = align256(o + (size_t)hq * w.pre_blocks * 4);
@@ -646,19 +651,22 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int fp32, hipStream_t stream) {
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int fp32, hipStream_t stream) {
-  const int ktiles = (a.f.max_k + DkvCfg<bf16, 64>::BNB - 1) / DkvCfg<bf16, 64>::BNB;
-  if (ktiles == 0) return hipSuccess;
-  dim3 grid(a.f.hkv * a.splits * a.f.num_seqs, (ktiles + 1) / 2);
+  auto launch = [&](auto kernel, int bnb, int threads) {
+    const int ktiles = (a.f.max_k + bnb - 1) / bnb;
+    if (ktiles == 0) return;
+    dim3 grid(a.f.hkv * a.splits * a.f.num_seqs, (ktiles + 1) / 2);
+    hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, stream, a);
+  };
   if (a.f.d == 128) {
     if (fp32)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<float, 128>), grid, dim3(256), 0, stream, a);
+      launch(bwd_dkdv_kernel<float, 128>, DkvCfg<float, 128>::BNB, DkvCfg<float, 128>::THREADS);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<bf16, 128>), grid, dim3(256), 0, stream, a);
+      launch(bwd_dkdv_kernel<bf16, 128>, DkvCfg<bf16, 128>::BNB, DkvCfg<bf16, 128>::THREADS);
   } else {
     if (fp32)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<float, 64>), grid, dim3(256), 0, stream, a);
+      launch(bwd_dkdv_kernel<float, 64>, DkvCfg<float, 64>::BNB, DkvCfg<float, 64>::THREADS);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<bf16, 64>), grid, dim3(256), 0, stream, a);
+      launch(bwd_dkdv_kernel<bf16, 64>, DkvCfg<bf16, 64>::BNB, DkvCfg<bf16, 64>::THREADS);
   }
   return hipGetLastError();
 }

@@ -34,7 +34,11 @@ def test_head_dim_128_is_accepted(lib):
     n128 = lib.attn_sink_bwd_workspace_bytes(ctypes.byref(s))
     s64 = _shape(num_heads_q=64, num_heads_kv=8, total_q=4096, total_k=4096, max_seqlen_q=4096, max_seqlen_k=4096)
     n64 = lib.attn_sink_bwd_workspace_bytes(ctypes.byref(s64))
-    assert n128 - n64 == 2 * 4 * 4096 * 8 * 64 * 4  # the dK/dV partials double (4 splits)
+    # d=64: 4 head splits (512 workgroups, two per compute unit); d=128: one
+    # workgroup per compute unit fits, so 2 splits (256 workgroups)
+    fixed = 64 * 2 * 4096 * 4 + 64 * (4096 // 128) * 4
+    assert fixed + 2 * 4 * 4096 * 8 * 64 * 4 <= n64 <= fixed + 2 * 4 * 4096 * 8 * 64 * 4 + 4 * 256
+    assert fixed + 2 * 2 * 4096 * 8 * 128 * 4 <= n128 <= fixed + 2 * 2 * 4096 * 8 * 128 * 4 + 4 * 256
     assert lib.attn_sink_bwd(ctypes.byref(s), *[FAKE] * 11, FAKE, n128 - 1, None) == als.ERR_WORKSPACE
     d = _decode_shape(head_dim=128)
     assert lib.attn_sink_fwd_decode_workspace_bytes(ctypes.byref(d)) > 0
