@@ -178,7 +178,7 @@ size_t attn_sink_bwd_workspace_bytes(const attn_sink_shape* shape) {
   if (check_shape(shape) != ATTN_SINK_OK) return 0;
   return bwd_workspace_layout(shape->num_heads_q, shape->num_heads_kv, shape->total_q, shape->total_k, shape->num_seqs,
                               shape->max_seqlen_q, shape->causal, shape->window > 0 ? shape->window : 0,
-                              shape->head_dim).total;
+                              shape->head_dim, shape->dtype == ATTN_SINK_FP32).total;
 }
 
 attn_sink_status attn_sink_bwd(const attn_sink_shape* shape, const void* q, const void* k, const void* v,
@@ -193,7 +193,7 @@ attn_sink_status attn_sink_bwd(const attn_sink_shape* shape, const void* q, cons
   if (any_k && (!k || !v || !dk || !dv)) return ATTN_SINK_ERR_INVALID_ARG;
   const BwdWorkspace ws = bwd_workspace_layout(shape->num_heads_q, shape->num_heads_kv, shape->total_q, shape->total_k, shape->num_seqs,
                               shape->max_seqlen_q, shape->causal, shape->window > 0 ? shape->window : 0,
-                              shape->head_dim);
+                              shape->head_dim, shape->dtype == ATTN_SINK_FP32);
   if (!workspace || workspace_bytes < ws.total || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
     return ATTN_SINK_ERR_WORKSPACE;
 

@@ -74,8 +74,8 @@ struct BwdWorkspace {
   int pre_blocks, splits;
 };
 BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k, int num_seqs, int max_q, int causal,
-                                  int window, int d);
-int bwd_head_splits(int hq, int hkv, int total_k, int num_seqs, int causal, int window, int d);
+                                  int window, int d, int fp32);
+int bwd_head_splits(int hq, int hkv, int total_k, int num_seqs, int causal, int window, int d, int fp32);
 
 struct DecodeWorkspace {
   size_t part_o, part_ml, total;
