@@ -297,6 +297,11 @@ __global__ __launch_bounds__((DkvCfg<T, D>::THREADS), (sizeof(T) == 2 && D == 64
   const int nkt = (nk + C::BNB - 1) / C::BNB;
   const int fold = blockIdx.y;
   if (fold >= (nkt + 1) / 2) return;
+  // Two workgroups share a compute unit here, and the wavefront arbiter favours the older
+  // one, which runs about a quarter faster; the pair then ends apart and the later one
+  // runs alone. Workgroups of the second half of the grid (the younger of each pair)
+  // raise their wavefront priority on two steps of every three to even the two out.
+  const bool young = DkvCfg<T, D>::PER_CU == 2 && 2 * fold >= (int)gridDim.y;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index (uniform)
@@ -462,6 +467,9 @@ __global__ __launch_bounds__((DkvCfg<T, D>::THREADS), (sizeof(T) == 2 && D == 64
     auto step = [&](int it, int qt, auto full_tag) __device__ {
       constexpr bool FULL = decltype(full_tag)::value;
       const int buf = it % NB;
+      if constexpr (DkvCfg<T, D>::PER_CU == 2) {
+        if (young && (it % 3 != 0)) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
+      }
       // bf16: tile it+2 goes to the buffer read in the previous step; fp32: tile it+1.
       const bool more = it + NB - 1 < n_it;
       if (more) stage(it + NB - 1, (it + NB - 1) % NB);
