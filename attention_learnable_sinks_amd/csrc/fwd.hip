@@ -151,7 +151,10 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
     }
   };
   // P = exp2(s * sl2 + neg_m) in place, rounded into operands; returns the lane's
-  // sum of the rounded P (the values that multiply V).
+  // sum of P in fp32, taken before the rounding.  The sum uses plain fp32 adds:
+  // the bf16 dot-product instruction that could sum the rounded operands directly
+  // does not overlap with the MFMAs of the other wavefronts on the SIMD, while
+  // adds do (measured: about 0.15 against 0.55 overlap).
   auto probs = [&](f32x16* st, Frag* pf, float neg_m) __attribute__((always_inline)) -> float {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -160,8 +163,15 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
     float sum = 0.f;
 #pragma unroll
     for (int s = 0; s < NP; ++s) {
-      pf[s] = pack_frag<T>(st, s);
-      sum = frag_sum<T>(pf[s], sum);
+      if constexpr (sizeof(T) == 2) {
+        const int r0 = 8 * (s % 2);
+        const f32x16& x = st[s / 2];
+        sum += ((x[r0] + x[r0 + 1]) + (x[r0 + 2] + x[r0 + 3])) + ((x[r0 + 4] + x[r0 + 5]) + (x[r0 + 6] + x[r0 + 7]));
+        pf[s] = pack_frag<T>(st, s);
+      } else {
+        pf[s] = pack_frag<T>(st, s);
+        sum = frag_sum<T>(pf[s], sum);
+      }
     }
     return sum;
   };
