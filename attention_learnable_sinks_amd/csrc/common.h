@@ -158,7 +158,9 @@ template <>
 struct FragAddr<bf16> {
   uint32_t row_[4];     // bytes of (row c, logical column 16 s + 8 h), s = 0..3
   uint32_t col_[2][2];  // [j][md]: bytes of (row 8 j + 4 h + t/4, column 32 md + 16 (g&1) + 4 (t&3))
-  __device__ inline void init(int lane) {
+  // pin = false leaves the offsets to the optimiser, which may then recompute them
+  // rather than hold eight registers (a kernel at a tight register budget).
+  __device__ inline void init(int lane, bool pin = true) {
     const int h = lane >> 5, c = lane & 31, g = lane >> 4, t = lane & 15;
 #pragma unroll
     for (int s = 0; s < 4; ++s) row_[s] = 2u * (uint32_t)Tile<bf16>::off(c, 16 * s + 8 * h);
@@ -167,6 +169,7 @@ struct FragAddr<bf16> {
 #pragma unroll
       for (int md = 0; md < 2; ++md)
         col_[j][md] = 2u * (uint32_t)Tile<bf16>::off(8 * j + 4 * h + (t >> 2), 32 * md + 16 * (g & 1) + 4 * (t & 3));
+    if (!pin) return;
 #pragma unroll
     for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(row_[s]));
 #pragma unroll
@@ -191,7 +194,7 @@ struct FragAddr<bf16> {
 template <>
 struct FragAddr<float> {
   int lane_;
-  __device__ inline void init(int lane) { lane_ = lane; }
+  __device__ inline void init(int lane, bool = true) { lane_ = lane; }
   __device__ inline float row(const float* tile, int mt, int s) const {
     return lds_row_frag<float>(tile, 32 * mt + (lane_ & 31), 2 * s + (lane_ >> 5));
   }

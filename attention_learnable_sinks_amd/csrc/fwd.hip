@@ -48,11 +48,21 @@ struct FwdCfg {
   static constexpr int BN = 64;        // keys per tile
   static constexpr int THREADS = 256;  // 4 wavefronts x 32 rows
   static constexpr int TILE = tile_elems_d<T, D>(BN);
+  // bf16 at d = 64 runs four workgroups per compute unit (registers capped at 128),
+  // one wavefront of each per SIMD, and raises its wavefront priority while it
+  // issues MFMAs: a wavefront whose matrix work is ready goes first, and the
+  // exponentials of the others fill the cycles the matrix core leaves to the
+  // vector ALU.  The priority windows also bound how far the compiler hoists LDS
+  // reads, which keeps the kernel inside 128 registers without spilling.  Measured
+  // against three workgroups per compute unit without priority: 4k causal -6%,
+  // 16k window-128 layer -9 to -16%, 20k causal -2%.
+  static constexpr bool PACKED = sizeof(T) == 2 && D == 64;
+  static constexpr int MIN_WG = PACKED ? 4 : 1;
 };
 
 // D: head dim (64 or 128).
 template <typename T, int D>
-__global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
+__global__ __launch_bounds__(256, (FwdCfg<T, D>::MIN_WG)) void fwd_kernel(FwdArgs p) {
   using C = FwdCfg<T, D>;
   using M = Mfma<T>;
   using Frag = typename M::Frag;
@@ -116,7 +126,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
 
   const Span row_keys = keys_of_row(qi, off, nk, p.causal, p.window);  // the keys row qi sees
   FragAddr<T> fa;
-  fa.init(lane);
+  fa.init(lane, !C::PACKED);
   TileLoaderD<T, C::BN, C::THREADS, D> kld, vld;
   kld.init(kbase_p, kv_row, nk, tid);
   vld.init(vbase_p, kv_row, nk, tid);
@@ -133,6 +143,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
   // the tile straddles a band edge.
   auto scores = [&](f32x16* st, const T* Ks, int kbase, auto full_tag) __attribute__((always_inline)) {
     constexpr bool FULL = decltype(full_tag)::value;
+    if constexpr (C::PACKED) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
@@ -140,6 +151,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
 #pragma unroll
       for (int s = 0; s < D / KS; ++s) st[mt] = M::mma(frag_row<T, C::BN>(fa, Ks, mt, s), qf[s], st[mt]);
     }
+    if constexpr (C::PACKED) __builtin_amdgcn_s_setprio(0);
     if constexpr (!FULL) {
       // key of register r in tile mt: kbase + 4h + (32 mt + 8 (r/4) + r%4), a constant per element
       const int k0 = kbase + 4 * h;
@@ -210,10 +222,12 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
     }
     l_run += tsum;
     // O^T[d x q] += V^T[d x keys] . P^T[keys x q]
+    if constexpr (C::PACKED) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s = 0; s < NP; ++s)
 #pragma unroll
       for (int md = 0; md < D / 32; ++md) oacc[md] = M::mma(frag_col<T, C::BN>(fa, Vs, md, s), pf[s], oacc[md]);
+    if constexpr (C::PACKED) __builtin_amdgcn_s_setprio(0);
   };
   // One pipeline step: start loading tile kt+1 into the other buffer, compute tile
   // kt, wait for the load, barrier.  `cur` / `nxt` are the two buffers (K then V).
