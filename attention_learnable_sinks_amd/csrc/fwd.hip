@@ -54,8 +54,8 @@ struct FwdCfg {
   // exponentials of the others fill the cycles the matrix core leaves to the
   // vector ALU.  The priority windows also bound how far the compiler hoists LDS
   // reads, which keeps the kernel inside 128 registers without spilling.  Measured
-  // against three workgroups per compute unit without priority: 4k causal -6%,
-  // 16k window-128 layer -9 to -16%, 20k causal -2%.
+  // against three workgroups per compute unit without priority: 4k causal -0.5 to
+  // -1%, 20k causal -1 to -4%, window-128 layers -5%.
   static constexpr bool PACKED = sizeof(T) == 2 && D == 64;
   static constexpr int MIN_WG = PACKED ? 4 : 1;
 };
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::MIN_WG)) void fwd_kernel(FwdArg
   // sum of P in fp32, taken before the rounding.  The sum uses plain fp32 adds:
   // the bf16 dot-product instruction that could sum the rounded operands directly
   // does not overlap with the MFMAs of the other wavefronts on the SIMD, while
-  // adds do (measured: about 0.15 against 0.55 overlap).
+  // adds do (measured: about 0.15 against 0.55 overlap); about 1% faster here.
   auto probs = [&](f32x16* st, Frag* pf, float neg_m) __attribute__((always_inline)) -> float {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
