@@ -17,6 +17,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -33,11 +34,19 @@ KERNEL_SOURCES = ["attention_learnable_sinks_amd/csrc/common.h", "attention_lear
 DECODE_SOURCES = ["attention_learnable_sinks_amd/csrc/common.h", "attention_learnable_sinks_amd/csrc/decode.hip"]
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments, blank lines or trailing blanks: an edit to a
+    comment leaves the kernel, and the digest, unchanged."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*$", "", line).rstrip() for line in text.splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def source_digest(paths=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
