@@ -245,13 +245,15 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # K steps with the library's per-kernel HIP events recorded on the launch stream:
-    # the per-launch durations of the roofline.  The event records add about 25 us of
-    # queue markers per step, so `value` comes from the next, uninstrumented pass.
+    # Steps with the library's per-kernel HIP events recorded on the launch stream: the
+    # per-launch durations of the roofline.  The event records add about 25 us of queue
+    # markers per step, so `value` comes from the next, uninstrumented pass.  At least
+    # 40 steps, so the GPU has settled before that pass even with a short warm-up.
+    n_ev = max(args.steps, 40)
     als.timing_enable(True)
     torch.cuda.synchronize()
     t2 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(n_ev):
         step()
     torch.cuda.synchronize()
     t3 = time.perf_counter()
@@ -340,7 +342,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
-        "ms_per_step_with_kernel_events": round((t3 - t2) * 1e3 / args.steps, 5),
+        "ms_per_step_with_kernel_events": round((t3 - t2) * 1e3 / n_ev, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
