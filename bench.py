@@ -69,6 +69,29 @@ def read_traffic(workload: str, kernel: str):
         return None
 
 
+def read_sclk(workload: str, kernel: str):
+    """Core clock (GHz) the kernel ran at in the committed counter run (an upper bound:
+    the busy counter includes some cycles outside the kernel), or None when there is none
+    or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    digest, clocks = None, {}
+    for line in open(path):
+        parts = line.split()
+        if line.startswith("kernel_source_digest") and len(parts) > 1:
+            digest = parts[1]
+        elif line.startswith("sclk_ghz") and len(parts) == 3:
+            clocks[parts[1]] = float(parts[2])
+    if digest != source_digest(KERNEL_SOURCES):
+        return None
+    short = kernel.replace("attn_sink_", "")  # attn_sink_bwd_dkdv_kernel -> bwd_dkdv_kernel
+    for name, ghz in clocks.items():
+        if short in name and "DF16bLi64" in name:
+            return ghz
+    return None
+
+
 def count_pairs(seqlens, causal: bool, window: int) -> int:
     """Visible (query, key) pairs per query head: the work unit of the FLOP count."""
     total = 0
@@ -323,6 +346,15 @@ def main():
     roofline = dict(bound=bound, achieved=round(achieved, 3), peak=peak, unit=unit, frac=round(achieved / peak, 4),
                     traffic=read_traffic(args.workload, dom), kernel=dom, launch_ms=round(per[dom], 5),
                     flop_per_byte=round(flop / max(byts, 1), 1))
+    # The same against the clock the kernel actually ran at (CUs x 4096 bf16 FLOP per clock x
+    # the core clock from the committed counter run, an upper bound, so this fraction is a
+    # lower bound).
+    sclk = read_sclk(args.workload, dom) if bound == "mfma" and w.dtype == "bf16" else None
+    if sclk is not None:
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        adj = cus * 4096 * sclk * 1e9 / 1e12
+        roofline.update(sclk_ghz=sclk, clock_adjusted_peak=round(adj, 1),
+                        frac_of_clock_adjusted_peak=round(achieved / adj, 4))
     fwd_bytes = kern_bytes["attn_sink_fwd_kernel"]
     bwd_bytes = 3 * qb + 2 * kb + rows + qb + 2 * kb + rows  # Q K V O dO LSE -> dQ dK dV, plus D (37,376 B per token at 64/8 heads)
 
