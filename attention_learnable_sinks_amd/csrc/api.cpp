@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdint>
+#include <initializer_list>
 #include <mutex>
 #include <vector>
 
@@ -67,6 +69,16 @@ attn_sink_status timed_launch(int kernel, hipStream_t stream, F&& launch) {
   return ATTN_SINK_OK;
 }
 
+// Tensor pointers the kernels access in 16-byte pieces, and 4-byte scalar arrays.
+// A null pointer passes here; the null checks of each entry point come first.
+bool misaligned(std::initializer_list<const void*> wide, std::initializer_list<const void*> narrow) {
+  for (const void* p : wide)
+    if (reinterpret_cast<uintptr_t>(p) & 15) return true;
+  for (const void* p : narrow)
+    if (reinterpret_cast<uintptr_t>(p) & 3) return true;
+  return false;
+}
+
 attn_sink_status check_shape(const attn_sink_shape* s) {
   if (!s) return ATTN_SINK_ERR_INVALID_ARG;
   if (s->dtype != ATTN_SINK_BF16 && s->dtype != ATTN_SINK_FP32) return ATTN_SINK_ERR_UNSUPPORTED;
@@ -76,6 +88,7 @@ attn_sink_status check_shape(const attn_sink_shape* s) {
   if (s->num_seqs < 1 || s->total_q < 0 || s->total_k < 0 || s->max_seqlen_q < 0 || s->max_seqlen_k < 0)
     return ATTN_SINK_ERR_INVALID_ARG;
   if (!s->cu_seqlens_q || !s->cu_seqlens_k) return ATTN_SINK_ERR_INVALID_ARG;
+  if (misaligned({}, {s->cu_seqlens_q, s->cu_seqlens_k})) return ATTN_SINK_ERR_INVALID_ARG;
   if (!(s->softmax_scale > 0.f) || !std::isfinite(s->softmax_scale)) return ATTN_SINK_ERR_INVALID_ARG;
   if (s->causal != 0 && s->causal != 1) return ATTN_SINK_ERR_INVALID_ARG;
   // grid limits: y is the tile index (<= 65535); x is heads * sequences
@@ -135,6 +148,7 @@ attn_sink_status attn_sink_fwd(const attn_sink_shape* shape, const void* q, cons
   if (st != ATTN_SINK_OK) return st;
   const bool any_q = shape->total_q > 0, any_k = shape->total_k > 0;
   if (!sinks || (any_q && (!q || !o || !lse)) || (any_k && (!k || !v))) return ATTN_SINK_ERR_INVALID_ARG;
+  if (misaligned({q, k, v, o}, {sinks, lse})) return ATTN_SINK_ERR_INVALID_ARG;
   if (!any_q) return ATTN_SINK_OK;
   FwdArgs a = fwd_args(shape, q, k, v, sinks, o, lse);
   const int fp32 = shape->dtype == ATTN_SINK_FP32;
@@ -155,6 +169,7 @@ attn_sink_status attn_sink_fwd_decode(const attn_sink_shape* shape, const void* 
   if (!decode_supported(shape->num_heads_q, shape->num_heads_kv, shape->max_seqlen_q)) return ATTN_SINK_ERR_UNSUPPORTED;
   const bool any_q = shape->total_q > 0, any_k = shape->total_k > 0;
   if (!sinks || (any_q && (!q || !o || !lse)) || (any_k && (!k || !v))) return ATTN_SINK_ERR_INVALID_ARG;
+  if (misaligned({q, k, v, o}, {sinks, lse})) return ATTN_SINK_ERR_INVALID_ARG;
   const DecodeWorkspace ws = decode_layout(shape);
   if (!workspace || workspace_bytes < ws.total || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
     return ATTN_SINK_ERR_WORKSPACE;
@@ -191,6 +206,7 @@ attn_sink_status attn_sink_bwd(const attn_sink_shape* shape, const void* q, cons
   if (!sinks || !dsinks) return ATTN_SINK_ERR_INVALID_ARG;
   if (any_q && (!q || !o || !lse || !dout || !dq)) return ATTN_SINK_ERR_INVALID_ARG;
   if (any_k && (!k || !v || !dk || !dv)) return ATTN_SINK_ERR_INVALID_ARG;
+  if (misaligned({q, k, v, o, dout, dq, dk, dv}, {sinks, lse, dsinks})) return ATTN_SINK_ERR_INVALID_ARG;
   const BwdWorkspace ws = bwd_workspace_layout(shape->num_heads_q, shape->num_heads_kv, shape->total_q, shape->total_k, shape->num_seqs,
                               shape->max_seqlen_q, shape->causal, shape->window > 0 ? shape->window : 0,
                               shape->head_dim, shape->dtype == ATTN_SINK_FP32);
@@ -232,6 +248,7 @@ attn_sink_status attn_sink_merge(int dtype, int head_dim, int num_heads_q, int t
   if (num_heads_q < 1 || total_q < 0 || num_parts < 1) return ATTN_SINK_ERR_INVALID_ARG;
   if (!sinks) return ATTN_SINK_ERR_INVALID_ARG;
   if (total_q > 0 && (!o_parts || !lse_parts || !o || !lse)) return ATTN_SINK_ERR_INVALID_ARG;
+  if (misaligned({o_parts, o}, {lse_parts, sinks, lse})) return ATTN_SINK_ERR_INVALID_ARG;
   if (total_q == 0) return ATTN_SINK_OK;
   MergeArgs a;
   a.o_parts = o_parts;

@@ -31,6 +31,11 @@
  *   sinks, dsinks  : [Hq] float32, in score units (not multiplied by softmax_scale)
  *   cu_seqlens_q/k : [num_seqs + 1] int32, DEVICE memory, cu[0] = 0, nondecreasing,
  *                    cu[num_seqs] = total.  Fixed-length batches use [0, N, 2N, ...].
+ * Alignment: the kernels move q, k, v, o, dout, dq, dk, dv (and the merge's o_parts)
+ * in 16-byte pieces, so these pointers must be 16-byte aligned; the float32 and
+ * int32 arrays need their natural 4 bytes.  A misaligned pointer is
+ * ATTN_SINK_ERR_INVALID_ARG.  Whole allocations and row slices of contiguous
+ * tensors always qualify.
  *
  * Ownership: the caller allocates every buffer (device memory for all tensors,
  * including the backward workspace).  The library allocates no device memory,
@@ -62,7 +67,7 @@ extern "C" {
 
 typedef enum {
   ATTN_SINK_OK = 0,
-  ATTN_SINK_ERR_INVALID_ARG = 1,  /* null pointer, bad count, Hq % Hkv != 0, ... */
+  ATTN_SINK_ERR_INVALID_ARG = 1,  /* null or misaligned pointer, bad count, Hq % Hkv != 0, ... */
   ATTN_SINK_ERR_UNSUPPORTED = 2,  /* well-formed but not built: head_dim not 64 or 128, dtype, decode width */
   ATTN_SINK_ERR_WORKSPACE = 3,    /* workspace missing, misaligned or smaller than required */
   ATTN_SINK_ERR_HIP = 4           /* the HIP runtime refused a launch */

@@ -256,3 +256,56 @@ def test_timing_read_without_records(lib):
 def test_load_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="not found"):
         als.load(str(tmp_path / "missing.so"))
+
+
+# Pointer alignment: 16 bytes for the tensors the kernels move in 16-byte pieces,
+# 4 bytes for the float32 / int32 arrays.  Argument order of each entry point:
+#   fwd, fwd_decode: q k v sinks o lse        bwd: q k v sinks o lse dout dq dk dv dsinks
+WIDE_FWD, NARROW_FWD = (0, 1, 2, 4), (3, 5)
+WIDE_BWD, NARROW_BWD = (0, 1, 2, 4, 6, 7, 8, 9), (3, 5, 10)
+
+
+def _offset(n, slot, by):
+    ptrs = [FAKE] * n
+    ptrs[slot] = FAKE + by
+    return ptrs
+
+
+@pytest.mark.parametrize("slot,by", [(s, 8) for s in WIDE_FWD] + [(s, 2) for s in NARROW_FWD])
+def test_fwd_rejects_misaligned_tensor(lib, slot, by):
+    s = _shape()
+    assert lib.attn_sink_fwd(ctypes.byref(s), *_offset(6, slot, by), None) == als.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("slot,by", [(s, 8) for s in WIDE_BWD] + [(s, 2) for s in NARROW_BWD])
+def test_bwd_rejects_misaligned_tensor(lib, slot, by):
+    s = _shape()
+    assert lib.attn_sink_bwd(ctypes.byref(s), *_offset(11, slot, by), FAKE, 1 << 40, None) == als.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("slot,by", [(s, 8) for s in WIDE_FWD] + [(s, 2) for s in NARROW_FWD])
+def test_fwd_decode_rejects_misaligned_tensor(lib, slot, by):
+    s = _decode_shape()
+    ptrs = _offset(6, slot, by)
+    assert lib.attn_sink_fwd_decode(ctypes.byref(s), *ptrs, FAKE, 1 << 40, None) == als.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("slot", range(6))
+def test_fwd_decode_accepts_minimal_alignment(lib, slot):
+    """16 bytes (tensors) and 4 bytes (float32 arrays) pass the pointer check: the call
+    goes on to the workspace check, which a zero-byte workspace fails."""
+    s = _decode_shape()
+    ptrs = _offset(6, slot, 16 if slot in WIDE_FWD else 4)
+    assert lib.attn_sink_fwd_decode(ctypes.byref(s), *ptrs, FAKE, 0, None) == als.ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("slot,by", [(0, 8), (3, 8), (1, 2), (2, 2), (4, 2)])
+def test_merge_rejects_misaligned_tensor(lib, slot, by):
+    # o_parts lse_parts sinks o lse
+    assert lib.attn_sink_merge(als.FP32, 64, 8, 10, 3, *_offset(5, slot, by), None) == als.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("field", ["cu_seqlens_q", "cu_seqlens_k"])
+def test_rejects_misaligned_cu_seqlens(lib, field):
+    s = _shape(**{field: FAKE + 2})
+    assert lib.attn_sink_fwd(ctypes.byref(s), *[FAKE] * 6, None) == als.ERR_INVALID_ARG

@@ -42,6 +42,7 @@ SMALL = [
     ([257], 4, 2, False, 0, ("normal",)),
     ([190, 450], 4, 4, False, 100, ("uniform", -2.0, 8.0)),
     ([513], 16, 2, True, 128, ("normal",)),
+    ([300], 16, 1, True, 0, ("normal",)),  # one kv head: dK/dV over 16 head splits
 ]
 
 
