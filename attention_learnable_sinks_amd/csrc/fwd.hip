@@ -30,6 +30,10 @@
 //   * Longest query tiles are dispatched first (causal load balance), and the
 //     query heads that share a kv head are placed on one XCD so their K/V tiles
 //     hit the same L2.
+//   * Sliding-window layers whose sequences all have one length pack the query
+//     heads of a kv head into the rows of a tile (positions x heads): a tile then
+//     spans fewer positions and visits fewer key tiles, and the heads share every
+//     K/V tile it loads.
 #include <type_traits>
 
 #include "common.h"
@@ -61,7 +65,7 @@ struct FwdCfg {
 };
 
 // D: head dim (64 or 128).
-template <typename T, int D>
+template <typename T, int D, bool PKH>
 __global__ __launch_bounds__(256, (FwdCfg<T, D>::MIN_WG)) void fwd_kernel(FwdArgs p) {
   using C = FwdCfg<T, D>;
   using M = Mfma<T>;
@@ -70,27 +74,33 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::MIN_WG)) void fwd_kernel(FwdArg
   constexpr int NP = C::BN / KS;  // operand steps over the keys of a tile
   __shared__ __attribute__((aligned(16))) T smem[4 * C::TILE];  // [buf][K, V]
 
-  const XcdSlot slot = xcd_slot(blockIdx.x, p.hkv, p.hq / p.hkv);
+  // PKH (head-packed tiles, for sliding-window layers): the 128 rows of a tile are
+  // BM / G query positions x the G query heads of one kv head, row r = position
+  // r / G, head r % G.  A window tile then spans BM / G positions instead of BM, so
+  // it visits fewer key tiles, and the G heads share each K/V tile it loads.
+  const int G = p.hq / p.hkv;
+  const XcdSlot slot = xcd_slot(blockIdx.x, p.hkv, PKH ? 1 : G);
   const int b = slot.seq, g = slot.kv;
-  const int head = g * (p.hq / p.hkv) + slot.item;
   const int tile = gridDim.y - 1 - blockIdx.y;  // longest causal tiles first
+  const int bmq = PKH ? C::BM / G : C::BM;     // query positions per workgroup
 
   const SeqBounds sq = seq_bounds(p.cu_q, b, p.total_q);
   const SeqBounds sk = seq_bounds(p.cu_k, b, p.total_k);
   const int nq = sq.len, nk = sk.len, off = nk - nq;
-  const int qs = tile * C::BM;
+  const int qs = tile * bmq;
   if (qs >= nq) return;
-  const int qe = min(qs + C::BM, nq);
+  const int qe = min(qs + bmq, nq);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index (uniform)
   const int h = lane >> 5, c = lane & 31;
+  const int head = PKH ? g * G + (32 * w + c) % G : g * G + slot.item;  // this lane's row's head
 
   // Key range of the workgroup and of this wavefront.
   const int khi = p.causal ? clampi(qe - 1 + off + 1, 0, nk) : nk;
   const int klo = p.window > 0 ? clampi(qs + off - p.window + 1, 0, nk) : 0;
-  const int qw = qs + 32 * w;
-  const int qw_end = min(qw + 32, nq);
+  const int qw = PKH ? qs + (32 * w) / G : qs + 32 * w;                    // first position of the wavefront
+  const int qw_end = min(PKH ? qs + (32 * w + 31) / G + 1 : qw + 32, nq);  // one past its last
   const bool wave_rows = qw < nq;
   int whi = p.causal ? clampi(qw_end - 1 + off + 1, 0, nk) : nk;
   int wlo = p.window > 0 ? clampi(qw + off - p.window + 1, 0, nk) : 0;
@@ -101,7 +111,7 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::MIN_WG)) void fwd_kernel(FwdArg
   const T* vbase_p = static_cast<const T*>(p.v) + (size_t)sk.start * kv_row + g * D;
 
   // Q fragments (B operand of S^T = K Q^T): lane owns query qw + c, d = KS*s + E*h + e.
-  const int qi = qw + c;
+  const int qi = PKH ? qs + (32 * w + c) / G : qw + c;  // this lane's row's position
   typename M::Frag qf[D / KS];
   {
     const bool ok = qi < nq;
@@ -311,20 +321,48 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::MIN_WG)) void fwd_kernel(FwdArg
   }
 }
 
+// Head-packed tiles (they need G | BM and G > 1) on sliding-window layers whose
+// sequences all have max_q rows.  A tile of BM positions visits about
+// (BM + window) / BN key tiles, one of BM / G positions about (BM / G + window) / BN.
+// Measured at window 128, G = 8 (GPT-OSS shapes): one 16k sequence 107 against
+// 121 us, one 49.8k sequence 304 against 341, eight of 6225 rows 311 against 356;
+// the ragged batch of eight (1,277 to 14,090 rows, 49.8k in all) 443 against 356,
+// for a reason not found (not the grid's empty tiles, not the dispatch order), so
+// ragged batches keep per-head tiles.  Both layouts give every row bitwise the
+// same result: a row's arithmetic does not depend on the other rows of its tile.
+static bool fwd_head_packed(const FwdArgs& a) {
+  const int G = a.hq / a.hkv;
+  if (a.window <= 0 || G < 2 || FwdCfg<bf16, 64>::BM % G != 0) return false;
+  if ((long long)a.max_q * a.num_seqs != a.total_q) return false;  // equal lengths only
+  const long long tiles = ((long long)a.max_q * G + FwdCfg<bf16, 64>::BM - 1) / FwdCfg<bf16, 64>::BM;
+  return tiles <= 65535;
+}
+
+template <typename T, int D>
+static void launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
+  constexpr int BM = FwdCfg<T, D>::BM;
+  if (fwd_head_packed(a)) {
+    const int bmq = BM / (a.hq / a.hkv);
+    dim3 grid(a.hkv * a.num_seqs, (a.max_q + bmq - 1) / bmq);
+    hipLaunchKernelGGL((fwd_kernel<T, D, true>), grid, dim3(256), 0, stream, a);
+  } else {
+    dim3 grid(a.hq * a.num_seqs, (a.max_q + BM - 1) / BM);
+    hipLaunchKernelGGL((fwd_kernel<T, D, false>), grid, dim3(256), 0, stream, a);
+  }
+}
+
 hipError_t launch_fwd(const FwdArgs& a, int fp32, hipStream_t stream) {
-  const int tiles = (a.max_q + FwdCfg<bf16, 64>::BM - 1) / FwdCfg<bf16, 64>::BM;
-  if (tiles == 0 || a.num_seqs == 0) return hipSuccess;
-  dim3 grid(a.hq * a.num_seqs, tiles);
+  if (a.max_q == 0 || a.num_seqs == 0) return hipSuccess;
   if (a.d == 128) {
     if (fp32)
-      hipLaunchKernelGGL((fwd_kernel<float, 128>), grid, dim3(256), 0, stream, a);
+      launch_fwd_t<float, 128>(a, stream);
     else
-      hipLaunchKernelGGL((fwd_kernel<bf16, 128>), grid, dim3(256), 0, stream, a);
+      launch_fwd_t<bf16, 128>(a, stream);
   } else {
     if (fp32)
-      hipLaunchKernelGGL((fwd_kernel<float, 64>), grid, dim3(256), 0, stream, a);
+      launch_fwd_t<float, 64>(a, stream);
     else
-      hipLaunchKernelGGL((fwd_kernel<bf16, 64>), grid, dim3(256), 0, stream, a);
+      launch_fwd_t<bf16, 64>(a, stream);
   }
   return hipGetLastError();
 }

@@ -24,6 +24,7 @@ CASES = [
     ([333, 64, 200], 4, 4, True, 37),
     ([257], 4, 2, False, 0),
     ([190, 450], 4, 4, False, 100),
+    ([300], 8, 2, True, 64),  # one sequence, window: head-packed forward tiles
 ]
 
 
