@@ -30,10 +30,9 @@
 //   * Longest query tiles are dispatched first (causal load balance), and the
 //     query heads that share a kv head are placed on one XCD so their K/V tiles
 //     hit the same L2.
-//   * Sliding-window layers whose sequences all have one length pack the query
-//     heads of a kv head into the rows of a tile (positions x heads): a tile then
-//     spans fewer positions and visits fewer key tiles, and the heads share every
-//     K/V tile it loads.
+//   * Sliding-window layers pack the query heads of a kv head into the rows of a
+//     tile (positions x heads): a tile then spans fewer positions and visits fewer
+//     key tiles, and the heads share every K/V tile it loads.
 #include <type_traits>
 
 #include "common.h"
@@ -80,9 +79,15 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::MIN_WG)) void fwd_kernel(FwdArg
   // it visits fewer key tiles, and the G heads share each K/V tile it loads.
   const int G = p.hq / p.hkv;
   const XcdSlot slot = xcd_slot(blockIdx.x, p.hkv, PKH ? 1 : G);
-  const int b = slot.seq, g = slot.kv;
-  const int tile = gridDim.y - 1 - blockIdx.y;  // longest causal tiles first
   const int bmq = PKH ? C::BM / G : C::BM;     // query positions per workgroup
+  // Packed: blockIdx.y = sequence x its tiles (sequence-major), so the workgroups one XCD
+  // receives are consecutive tiles of one sequence.  (Tile-major, one XCD receives one
+  // workgroup per sequence in turn; where only the longest sequence still has tiles, the
+  // working workgroups recur with the period of the batch size and the ragged batch above
+  // ran 23% slower than per-head tiles.)  Per-head: longest causal tiles first.
+  const int pk_tiles = PKH ? (p.max_q + bmq - 1) / bmq : 1;
+  const int b = PKH ? (int)blockIdx.y / pk_tiles : slot.seq, g = slot.kv;
+  const int tile = PKH ? (int)blockIdx.y % pk_tiles : gridDim.y - 1 - blockIdx.y;
 
   const SeqBounds sq = seq_bounds(p.cu_q, b, p.total_q);
   const SeqBounds sk = seq_bounds(p.cu_k, b, p.total_k);
@@ -321,21 +326,18 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::MIN_WG)) void fwd_kernel(FwdArg
   }
 }
 
-// Head-packed tiles (they need G | BM and G > 1) on sliding-window layers whose
-// sequences all have max_q rows.  A tile of BM positions visits about
-// (BM + window) / BN key tiles, one of BM / G positions about (BM / G + window) / BN.
-// Measured at window 128, G = 8 (GPT-OSS shapes): one 16k sequence 107 against
-// 121 us, one 49.8k sequence 304 against 341, eight of 6225 rows 311 against 356;
-// the ragged batch of eight (1,277 to 14,090 rows, 49.8k in all) 443 against 356,
-// for a reason not found (not the grid's empty tiles, not the dispatch order), so
-// ragged batches keep per-head tiles.  Both layouts give every row bitwise the
-// same result: a row's arithmetic does not depend on the other rows of its tile.
+// Head-packed tiles (they need G | BM and G > 1) on sliding-window layers.  A tile
+// of BM positions visits about (BM + window) / BN key tiles, one of BM / G positions
+// about (BM / G + window) / BN.  Measured at window 128, G = 8 (GPT-OSS shapes),
+// against per-head tiles: one 16k sequence 105 against 115 us, eight of 6225 rows
+// 318 against 362, the ragged batch of eight (1,277 to 14,090 rows) 336 against
+// 369.  Both layouts give every row bitwise the same result: a row's arithmetic
+// does not depend on the other rows of its tile.
 static bool fwd_head_packed(const FwdArgs& a) {
   const int G = a.hq / a.hkv;
   if (a.window <= 0 || G < 2 || FwdCfg<bf16, 64>::BM % G != 0) return false;
-  if ((long long)a.max_q * a.num_seqs != a.total_q) return false;  // equal lengths only
   const long long tiles = ((long long)a.max_q * G + FwdCfg<bf16, 64>::BM - 1) / FwdCfg<bf16, 64>::BM;
-  return tiles <= 65535;
+  return tiles * a.num_seqs <= 65535;
 }
 
 template <typename T, int D>
@@ -343,7 +345,7 @@ static void launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   constexpr int BM = FwdCfg<T, D>::BM;
   if (fwd_head_packed(a)) {
     const int bmq = BM / (a.hq / a.hkv);
-    dim3 grid(a.hkv * a.num_seqs, (a.max_q + bmq - 1) / bmq);
+    dim3 grid(a.hkv, a.num_seqs * ((a.max_q + bmq - 1) / bmq));
     hipLaunchKernelGGL((fwd_kernel<T, D, true>), grid, dim3(256), 0, stream, a);
   } else {
     dim3 grid(a.hq * a.num_seqs, (a.max_q + BM - 1) / BM);

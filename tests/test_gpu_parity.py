@@ -186,29 +186,31 @@ def test_running_max_raised_mid_row(gpu_lib, dtype):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("hq,hkv,causal", [(16, 2, True), (16, 1, True), (8, 4, True), (16, 2, False)])
-def test_head_packed_tiles_match_per_head_tiles_bitwise(gpu_lib, dtype, hq, hkv, causal):
-    """Window layers whose sequences all have the same length run on tiles that pack
-    the query heads of a kv head (rows = positions x heads); ragged batches run on
-    per-head tiles.  A sequence computed alone (packed) and inside a ragged batch
-    (per-head) must give bitwise the same O and LSE: a row's arithmetic depends only
-    on its own scores, and key tiles sit at the same absolute key positions."""
+def test_head_packed_tiles_bitwise(gpu_lib, dtype, hq, hkv, causal):
+    """Window layers run on tiles that pack the query heads of a kv head (rows =
+    positions x heads); layers without a window run on per-head tiles.  A row's
+    arithmetic depends only on its own scores, with key tiles at the same absolute
+    key positions, so (1) a window of at least n keys (packed) gives bitwise the
+    per-head causal / full result, and (2) a sequence alone gives bitwise the rows
+    it gets inside a ragged batch."""
     n, m, window = 300, 77, 70
     inp = random_case([n, m], hq, hkv, 64, dtype, seed=hq + hkv + int(causal), causal=causal, window=window)
     d = to_dev(inp)
     sc = inp["softmax_scale"]
-    print(f"[case] packed vs per-head {dtype} {hq}x{hkv} causal={causal}", flush=True)
+    print(f"[case] head-packed {dtype} {hq}x{hkv} causal={causal}", flush=True)
     cu2 = torch.tensor([0, n, n + m], dtype=torch.int32, device="cuda")
-    o2, lse2 = gpu_lib.fwd(d["q"], d["k"], d["v"], d["sinks"], cu2, cu2, n, n, sc, causal, window)
     cu1 = torch.tensor([0, n], dtype=torch.int32, device="cuda")
     q, k, v = d["q"][:n].contiguous(), d["k"][:n].contiguous(), d["v"][:n].contiguous()
+    o_wide, lse_wide = gpu_lib.fwd(q, k, v, d["sinks"], cu1, cu1, n, n, sc, causal, n + 5)
+    o_none, lse_none = gpu_lib.fwd(q, k, v, d["sinks"], cu1, cu1, n, n, sc, causal, 0)
+    o2, lse2 = gpu_lib.fwd(d["q"], d["k"], d["v"], d["sinks"], cu2, cu2, n, n, sc, causal, window)
     o1, lse1 = gpu_lib.fwd(q, k, v, d["sinks"], cu1, cu1, n, n, sc, causal, window)
     torch.cuda.synchronize()
-    assert torch.equal(o1, o2[:n])
-    assert torch.equal(lse1, lse2[:, :n])
-    ref = oracle_bwd({**inp, "q": inp["q"][:n], "k": inp["k"][:n], "v": inp["v"][:n], "dout": inp["dout"][:n],
-                      "cu_seqlens": torch.tensor([0, n], dtype=torch.int32)})
-    compare({"o": o1.float().cpu().numpy().astype(np.float64), "lse": lse1.cpu().numpy().astype(np.float64)},
-            ref, ("o", "lse"), TOL[dtype], f"packed {dtype} {hq}x{hkv}")
+    assert torch.equal(o_wide, o_none) and torch.equal(lse_wide, lse_none)
+    assert torch.equal(o1, o2[:n]) and torch.equal(lse1, lse2[:, :n])
+    ref = oracle_bwd(inp)
+    compare({"o": o2.float().cpu().numpy().astype(np.float64), "lse": lse2.cpu().numpy().astype(np.float64)},
+            ref, ("o", "lse"), TOL[dtype], f"head-packed {dtype} {hq}x{hkv}")
 
 
 @pytest.mark.parametrize("window", [0, 50])
