@@ -47,40 +47,49 @@ struct DqCfg {
   static constexpr int TILE = tile_elems_d<T, D>(BN);
 };
 
-template <typename T, int D>
+template <typename T, int D, bool PKH>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   using C = DqCfg<T, D>;
   using M = Mfma<T>;
   constexpr int E = M::E, KS = M::KS;
   const FwdArgs& f = a.f;
   __shared__ __attribute__((aligned(16))) T smem[4 * C::TILE];  // [buf][K, V]
-  __shared__ float red[4];
+  __shared__ float red[PKH ? C::BM : 4];
 
-  const XcdSlot slot = xcd_slot(blockIdx.x, f.hkv, f.hq / f.hkv);
-  const int b = slot.seq, g = slot.kv;
-  const int head = g * (f.hq / f.hkv) + slot.item;
-  const int tile = gridDim.y - 1 - blockIdx.y;
-  const SeqBounds sq = seq_bounds(f.cu_q, b, f.total_q);
-  const SeqBounds sk = seq_bounds(f.cu_k, b, f.total_k);
-  const int nq = sq.len, nk = sk.len, off = nk - nq;
-  const int qs = tile * C::BM;
-  // This workgroup's slot of the dS_h partials (one per head, sequence and row tile).
-  float* const dsink_slot = a.dsink_part + (size_t)head * a.pre_blocks + (size_t)b * gridDim.y + tile;
-  if (qs >= nq) {
-    if (threadIdx.x == 0) *dsink_slot = 0.f;
-    return;
-  }
-  const int qe = min(qs + C::BM, nq);
-
+  // PKH (head-packed tiles, sliding-window layers): the 128 rows of a tile are
+  // BM / G positions x the G query heads of one kv head (row r: position r / G,
+  // head r % G), as in the forward; blockIdx.y = sequence x its tiles.
+  const int G = f.hq / f.hkv;
+  const XcdSlot slot = xcd_slot(blockIdx.x, f.hkv, PKH ? 1 : G);
+  const int bmq = PKH ? C::BM / G : C::BM;  // query positions per workgroup
+  const int ntiles = PKH ? (f.max_q + bmq - 1) / bmq : (int)gridDim.y;  // row tiles per sequence
+  const int b = PKH ? (int)blockIdx.y / ntiles : slot.seq, g = slot.kv;
+  const int tile = PKH ? (int)blockIdx.y % ntiles : gridDim.y - 1 - blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index (uniform)
   const int h = lane >> 5, c = lane & 31;
+  const int head = PKH ? g * G + (32 * w + c) % G : g * G + slot.item;  // this lane's row's head
+  const SeqBounds sq = seq_bounds(f.cu_q, b, f.total_q);
+  const SeqBounds sk = seq_bounds(f.cu_k, b, f.total_k);
+  const int nq = sq.len, nk = sk.len, off = nk - nq;
+  const int qs = tile * bmq;
+  // This workgroup's slot of the dS_h partials (one per head, sequence and row tile);
+  // packed: head g*G + j's slot is dsink_slot + j * pre_blocks.
+  float* const dsink_slot =
+      a.dsink_part + (size_t)(PKH ? g * G : head) * a.pre_blocks + (size_t)b * ntiles + tile;
+  if (qs >= nq) {
+    if (PKH ? tid < G : tid == 0) dsink_slot[(size_t)tid * a.pre_blocks] = 0.f;
+    return;
+  }
+  const int qe = min(qs + bmq, nq);
+
   FragAddr<T> fa;
   fa.init(lane);
   const int khi = f.causal ? clampi(qe - 1 + off + 1, 0, nk) : nk;
   const int klo = f.window > 0 ? clampi(qs + off - f.window + 1, 0, nk) : 0;
-  const int qw = qs + 32 * w;
-  const int qw_end = min(qw + 32, nq);
+  const int qw = PKH ? qs + (32 * w) / G : qs + 32 * w;                    // first position of the wavefront
+  const int qw_last = PKH ? qs + (32 * w + 31) / G : qw + 31;              // its last position
+  const int qw_end = min(qw_last + 1, nq);
   int whi = f.causal ? clampi(qw_end - 1 + off + 1, 0, nk) : nk;
   int wlo = f.window > 0 ? clampi(qw + off - f.window + 1, 0, nk) : 0;
   if (qw >= nq) whi = wlo = 0;
@@ -90,7 +99,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const T* vbase_p = static_cast<const T*>(f.v) + (size_t)sk.start * kv_row + g * D;
 
   // Q and dO fragments (B operands of S^T = K Q^T and dP^T = V dO^T); lse and D of the lane's row.
-  const int qi = qw + c;
+  const int qi = PKH ? qs + (32 * w + c) / G : qw + c;  // this lane's row's position
   const bool qok = qi < nq;
   Span row_keys = keys_of_row(qi, off, nk, f.causal, f.window);  // the keys row qi sees
   if (!qok) row_keys.len = 0u;
@@ -146,16 +155,29 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     const float sink = f.sinks[head];
     const float ps = (writer && lse > -INFINITY && sink > -INFINITY) ? fast_exp2((sink - lse) * kLog2e) : 0.f;
     float contrib = -ps * dd;
+    if constexpr (PKH) {
+      if (h == 0) red[32 * w + c] = contrib;  // by row; summed per head below
+    } else {
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) contrib += __shfl_xor(contrib, m);
-    if (lane == 0) red[w] = contrib;
+      for (int m = 32; m >= 1; m >>= 1) contrib += __shfl_xor(contrib, m);
+      if (lane == 0) red[w] = contrib;
+    }
   }
   f32x16 neg_dd;  // -D of the lane's row in every register
 #pragma unroll
   for (int r = 0; r < 16; ++r) neg_dd[r] = -dd;
   vmem_drain();
   __syncthreads();
-  if (tid == 0) *dsink_slot = (red[0] + red[1]) + (red[2] + red[3]);
+  if constexpr (PKH) {
+    // head g*G + tid: its rows tid, tid + G, ... in order
+    if (tid < G) {
+      float acc = 0.f;
+      for (int r = tid; r < C::BM; r += G) acc += red[r];
+      dsink_slot[(size_t)tid * a.pre_blocks] = acc;
+    }
+  } else {
+    if (tid == 0) *dsink_slot = (red[0] + red[1]) + (red[2] + red[3]);
+  }
 
   // One tile: S^T, dP^T, P^T, dS^T, dQ^T += K^T dS^T; FULL tiles need no mask.
   auto body = [&](const T* Ks, const T* Vs, int kbase, auto full_tag) {
@@ -227,7 +249,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   };
   // Tiles [wf_lo, wf_hi) are fully visible to all 32 rows of this wavefront.
   int wf_lo = kt_begin, wf_hi = kt_begin;
-  if (qw + 32 <= nq) {
+  if (qw_last < nq) {
     const int lo_key = f.window > 0 ? qw_end + off - f.window : 0;
     const int hi_key = f.causal ? min(qw + off + 1, nk) : nk;
     wf_lo = clampi(lo_key > 0 ? (lo_key + C::BN - 1) / C::BN : 0, kt_begin, kt_end);
@@ -552,8 +574,20 @@ __global__ __launch_bounds__(256) void bwd_finish_kernel(BwdArgs a) {
     // dS_h of head blockIdx.x: the preprocess partials, summed in a fixed order
     // (strided per thread, then a fixed butterfly and the four wavefronts in order).
     const float* part = a.dsink_part + (size_t)blockIdx.x * a.pre_blocks;
+    // Eight strides' loads are issued before their adds (0 past the end: acc is never
+    // -0, so adding +0 leaves it bitwise unchanged and the sum is that of the plain
+    // strided loop).
     float acc = 0.f;
-    for (int j = threadIdx.x; j < a.pre_blocks; j += blockDim.x) acc += part[j];
+    for (int j0 = threadIdx.x; j0 < a.pre_blocks; j0 += 8 * blockDim.x) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u * (int)blockDim.x;
+        v[u] = j < a.pre_blocks ? part[j] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += v[u];
+    }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
     __shared__ float red[4];
@@ -583,6 +617,22 @@ __global__ __launch_bounds__(256) void bwd_finish_kernel(BwdArgs a) {
 
 // ----------------------------------------------------------------------------- launchers
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Head-packed dQ tiles (as the forward's) on sliding-window layers: G = Hq / Hkv > 1
+// dividing the 128 rows of a tile, and the (sequence x tile) grid row within 65535.
+static bool dq_head_packed(int hq, int hkv, int num_seqs, int max_q, int window) {
+  constexpr int BM = DqCfg<bf16, 64>::BM;
+  const int G = hq / hkv;
+  if (window <= 0 || G < 2 || BM % G != 0) return false;
+  return ((long long)max_q * G + BM - 1) / BM * num_seqs <= 65535;
+}
+
+// Row tiles per sequence of the dQ grid (one dS_h partial per head and row tile).
+static int dq_tiles(int hq, int hkv, int num_seqs, int max_q, int window) {
+  constexpr int BM = DqCfg<bf16, 64>::BM;
+  const int per = dq_head_packed(hq, hkv, num_seqs, max_q, window) ? BM / (hq / hkv) : BM;
+  return (max_q + per - 1) / per;
+}
 
 int bwd_head_splits(int hq, int hkv, int total_k, int num_seqs, int causal, int window, int d, int fp32) {
   // The dK/dV grid has one workgroup per (sequence, kv head, head split, folded pair
@@ -628,7 +678,7 @@ BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k, int
                                   int window, int d, int fp32) {
   BwdWorkspace w;
   // one dS_h partial per (head, sequence, dQ row tile): the dQ workgroups write them
-  w.pre_blocks = num_seqs * ((max_q + DqCfg<bf16, 64>::BM - 1) / DqCfg<bf16, 64>::BM);
+  w.pre_blocks = num_seqs * dq_tiles(hq, hkv, num_seqs, max_q, window);
   w.splits = bwd_head_splits(hq, hkv, total_k, num_seqs, causal, window, d, fp32);
   size_t o = 0;
   w.rowstat = o;     o = align256(o + (size_t)hq * 2 * total_q * 4);
@@ -640,20 +690,28 @@ BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k, int
   return w;
 }
 
+template <typename T, int D>
+static void launch_bwd_dq_t(const BwdArgs& a, hipStream_t stream) {
+  const FwdArgs& f = a.f;
+  const int tiles = dq_tiles(f.hq, f.hkv, f.num_seqs, f.max_q, f.window);
+  if (dq_head_packed(f.hq, f.hkv, f.num_seqs, f.max_q, f.window))
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), dim3(f.hkv, f.num_seqs * tiles), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, false>), dim3(f.hq * f.num_seqs, tiles), dim3(256), 0, stream, a);
+}
+
 hipError_t launch_bwd_dq(const BwdArgs& a, int fp32, hipStream_t stream) {
-  const int tiles = (a.f.max_q + DqCfg<bf16, 64>::BM - 1) / DqCfg<bf16, 64>::BM;
-  if (tiles == 0) return hipSuccess;
-  dim3 grid(a.f.hq * a.f.num_seqs, tiles);
+  if (a.f.max_q == 0) return hipSuccess;
   if (a.f.d == 128) {
     if (fp32)
-      hipLaunchKernelGGL((bwd_dq_kernel<float, 128>), grid, dim3(256), 0, stream, a);
+      launch_bwd_dq_t<float, 128>(a, stream);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<bf16, 128>), grid, dim3(256), 0, stream, a);
+      launch_bwd_dq_t<bf16, 128>(a, stream);
   } else {
     if (fp32)
-      hipLaunchKernelGGL((bwd_dq_kernel<float, 64>), grid, dim3(256), 0, stream, a);
+      launch_bwd_dq_t<float, 64>(a, stream);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<bf16, 64>), grid, dim3(256), 0, stream, a);
+      launch_bwd_dq_t<bf16, 64>(a, stream);
   }
   return hipGetLastError();
 }

@@ -235,6 +235,13 @@ def test_workspace_size_formula(lib):
     n = lib.attn_sink_bwd_workspace_bytes(ctypes.byref(s))
     expect = hq * 2 * 16384 * 4 + hq * (16384 // 128) * 4  # 64 pairs x 8 = 512: no split, no partials
     assert expect <= n <= expect + 4 * 256
+    # window layer: dQ tiles pack the 8 query heads of a kv head (16 positions x 8 heads),
+    # so dS_h has one partial per head and 16-position tile; no dK/dV split at 16k
+    s = _shape(num_heads_q=64, num_heads_kv=8, total_q=16384, total_k=16384, max_seqlen_q=16384,
+               max_seqlen_k=16384, window=128)
+    n = lib.attn_sink_bwd_workspace_bytes(ctypes.byref(s))
+    expect = hq * 2 * 16384 * 4 + hq * (16384 // 16) * 4
+    assert expect <= n <= expect + 4 * 256
 
 
 def test_bwd_rejects_small_or_misaligned_workspace(lib):
