@@ -242,6 +242,12 @@ def test_workspace_size_formula(lib):
     n = lib.attn_sink_bwd_workspace_bytes(ctypes.byref(s))
     expect = hq * 2 * 16384 * 4 + hq * (16384 // 16) * 4
     assert expect <= n <= expect + 4 * 256
+    # two sequences: one partial per head, sequence and packed tile (still no dK/dV split)
+    s = _shape(num_heads_q=64, num_heads_kv=8, num_seqs=2, total_q=32768, total_k=32768, max_seqlen_q=16384,
+               max_seqlen_k=16384, window=128)
+    n = lib.attn_sink_bwd_workspace_bytes(ctypes.byref(s))
+    expect = hq * 2 * 32768 * 4 + hq * 2 * (16384 // 16) * 4
+    assert expect <= n <= expect + 4 * 256
 
 
 def test_bwd_rejects_small_or_misaligned_workspace(lib):
