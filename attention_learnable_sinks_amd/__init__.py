@@ -24,9 +24,7 @@ import torch
 __all__ = ["load", "fwd", "fwd_decode", "fwd_decode_workspace_bytes", "merge", "bwd", "bwd_workspace_bytes",
            "Shape", "AttnSinkError", "sink_attention", "timing_enable", "timing_read", "LIB_PATH"]
 
-# ATTN_SINK_LIBRARY may point at another build of the same library (e.g. a tuning variant).
-LIB_PATH = os.environ.get("ATTN_SINK_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
-                                                               "libattn_sink.so")
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_sink.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 BF16, FP32 = 0, 1
@@ -123,17 +121,36 @@ def make_shape(q: torch.Tensor, k: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_
                  softmax_scale=float(softmax_scale), causal=int(bool(causal)), window=int(window))
 
 
-def _check_tensors(q, k, v, sinks, cu_q, cu_k):
+def _check_buf(name, t, shape, dtype, device):
+    """A tensor the kernels read or write: exactly `shape`, `dtype`, contiguous, on `device`."""
+    if not isinstance(t, torch.Tensor) or t.device != device or tuple(t.shape) != tuple(shape) or \
+            t.dtype != dtype or not t.is_contiguous():
+        got = (tuple(t.shape), t.dtype, t.device, t.is_contiguous()) if isinstance(t, torch.Tensor) else type(t)
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {device}; got {got}")
+
+
+def _check_workspace(t, need, device):
+    if not isinstance(t, torch.Tensor) or t.device != device or t.dtype != torch.uint8 or t.dim() != 1 or \
+            not t.is_contiguous() or t.numel() < need:
+        raise ValueError(f"workspace must be a contiguous 1-d uint8 tensor of at least {need} bytes on {device}")
+
+
+def _check_tensors(q, k, v, sinks, cu_q, cu_k, device_type="cuda"):
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.dim() != 3 or not t.is_contiguous() or not t.is_cuda:
+        if not isinstance(t, torch.Tensor) or t.dim() != 3 or not t.is_contiguous() or t.device.type != device_type:
             raise ValueError(f"{name} must be a contiguous 3-d device tensor [T, H, d]")
+    dev = q.device
     if k.dtype != q.dtype or v.dtype != q.dtype or v.shape != k.shape or k.shape[2] != q.shape[2]:
         raise ValueError("q, k, v must share dtype and head dim; k and v must match")
-    if sinks.dtype != torch.float32 or sinks.numel() != q.shape[1] or not sinks.is_cuda or not sinks.is_contiguous():
-        raise ValueError("sinks must be a contiguous float32 device tensor [Hq]")
+    if k.device != dev or v.device != dev:
+        raise ValueError("q, k, v must be on one device")
+    _check_buf("sinks", sinks, (q.shape[1],), torch.float32, dev)
     for name, cu in (("cu_seqlens_q", cu_q), ("cu_seqlens_k", cu_k)):
-        if cu.dtype != torch.int32 or cu.dim() != 1 or not cu.is_cuda or not cu.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous int32 device tensor [num_seqs + 1]")
+        if not isinstance(cu, torch.Tensor) or cu.dtype != torch.int32 or cu.dim() != 1 or cu.device != dev or \
+                not cu.is_contiguous() or cu.numel() < 1:
+            raise ValueError(f"{name} must be a contiguous int32 tensor [num_seqs + 1] on {dev}")
+    if cu_q.numel() != cu_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length (num_seqs + 1)")
 
 
 def fwd(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
@@ -151,6 +168,8 @@ def fwd(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k=None, max_seqlen_q=None, max_
     shape = make_shape(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale, causal, window)
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty(q.shape[1], q.shape[0], dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_buf("out", o, q.shape, q.dtype, q.device)
+    _check_buf("lse", lse, (q.shape[1], q.shape[0]), torch.float32, q.device)
     st = _lib().attn_sink_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(o), _ptr(lse),
                               _stream(q.device))
     if st != OK:
@@ -177,10 +196,14 @@ def fwd_decode(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None, ma
     if softmax_scale is None:
         softmax_scale = q.shape[2] ** -0.5
     shape = make_shape(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale, causal, window)
+    need = fwd_decode_workspace_bytes(shape)
     if workspace is None:
-        workspace = torch.empty(max(fwd_decode_workspace_bytes(shape), 1), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, need, q.device)
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty(q.shape[1], q.shape[0], dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_buf("out", o, q.shape, q.dtype, q.device)
+    _check_buf("lse", lse, (q.shape[1], q.shape[0]), torch.float32, q.device)
     st = _lib().attn_sink_fwd_decode(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(o),
                                      _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                      _stream(q.device))
@@ -194,21 +217,23 @@ def merge(o_parts, lse_parts, sinks, out=None, lse=None):
     key shard) into sink attention, the sink counted once.  o_parts [P, Tq, Hq, 64]
     (bf16 or fp32), lse_parts [P, Hq, Tq] fp32, sinks [Hq] fp32, all contiguous on the
     device.  Returns (o [Tq, Hq, 64], lse [Hq, Tq])."""
-    if o_parts.dim() != 4 or not o_parts.is_contiguous() or not o_parts.is_cuda:
+    if not isinstance(o_parts, torch.Tensor) or o_parts.dim() != 4 or not o_parts.is_contiguous() or \
+            not o_parts.is_cuda:
         raise ValueError("o_parts must be a contiguous 4-d device tensor [P, Tq, Hq, d]")
     p, tq, hq, d = o_parts.shape
-    if lse_parts.shape != (p, hq, tq) or lse_parts.dtype != torch.float32 or not lse_parts.is_contiguous():
-        raise ValueError("lse_parts must be a contiguous float32 tensor [P, Hq, Tq]")
-    if sinks.dtype != torch.float32 or sinks.numel() != hq or not sinks.is_contiguous():
-        raise ValueError("sinks must be a contiguous float32 tensor [Hq]")
+    dev = o_parts.device
+    _check_buf("lse_parts", lse_parts, (p, hq, tq), torch.float32, dev)
+    _check_buf("sinks", sinks, (hq,), torch.float32, dev)
     if o_parts.dtype == torch.bfloat16:
         dt = BF16
     elif o_parts.dtype == torch.float32:
         dt = FP32
     else:
         raise TypeError(f"unsupported dtype {o_parts.dtype}")
-    o = torch.empty(tq, hq, d, dtype=o_parts.dtype, device=o_parts.device) if out is None else out
-    lse = torch.empty(hq, tq, dtype=torch.float32, device=o_parts.device) if lse is None else lse
+    o = torch.empty(tq, hq, d, dtype=o_parts.dtype, device=dev) if out is None else out
+    lse = torch.empty(hq, tq, dtype=torch.float32, device=dev) if lse is None else lse
+    _check_buf("out", o, (tq, hq, d), o_parts.dtype, dev)
+    _check_buf("lse", lse, (hq, tq), torch.float32, dev)
     st = _lib().attn_sink_merge(dt, d, hq, tq, p, _ptr(o_parts), _ptr(lse_parts), _ptr(sinks), _ptr(o), _ptr(lse),
                                 _stream(o_parts.device))
     if st != OK:
@@ -227,8 +252,8 @@ def bwd(q, k, v, sinks, o, lse, dout, cu_seqlens_q, cu_seqlens_k=None, max_seqle
     cu_seqlens_k = cu_seqlens_q if cu_seqlens_k is None else cu_seqlens_k
     _check_tensors(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k)
     for name, t in (("o", o), ("dout", dout)):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError(f"{name} must match q")
+        _check_buf(name, t, q.shape, q.dtype, q.device)
+    _check_buf("lse", lse, (q.shape[1], q.shape[0]), torch.float32, q.device)
     if max_seqlen_q is None:
         max_seqlen_q = int((cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max().item()) if cu_seqlens_q.numel() > 1 else 0
     if max_seqlen_k is None:
@@ -239,10 +264,13 @@ def bwd(q, k, v, sinks, o, lse, dout, cu_seqlens_q, cu_seqlens_k=None, max_seqle
     need = bwd_workspace_bytes(shape)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, need, q.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     dsinks = torch.empty_like(sinks) if dsinks is None else dsinks
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v), ("dsinks", dsinks, sinks)):
+        _check_buf(name, t, ref.shape, ref.dtype, q.device)
     st = _lib().attn_sink_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(o), _ptr(lse),
                               _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsinks), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _stream(q.device))

@@ -55,14 +55,21 @@ attn_sink_status timed_launch(int kernel, hipStream_t stream, F&& launch) {
     timing = g_timing;
   }
   Record rec{kernel, nullptr, nullptr};
+  // Events of a failed launch are released here (a recorded event may be destroyed
+  // before it completes; the runtime frees it once it has).
+  auto fail = [&rec]() {
+    if (rec.start) (void)hipEventDestroy(rec.start);
+    if (rec.stop) (void)hipEventDestroy(rec.stop);
+    return ATTN_SINK_ERR_HIP;
+  };
   if (timing) {
-    if (hipEventCreate(&rec.start) != hipSuccess || hipEventCreate(&rec.stop) != hipSuccess) return ATTN_SINK_ERR_HIP;
-    if (hipEventRecord(rec.start, stream) != hipSuccess) return ATTN_SINK_ERR_HIP;
+    if (hipEventCreate(&rec.start) != hipSuccess) return fail();
+    if (hipEventCreate(&rec.stop) != hipSuccess) return fail();
+    if (hipEventRecord(rec.start, stream) != hipSuccess) return fail();
   }
-  hipError_t e = launch();
-  if (e != hipSuccess) return ATTN_SINK_ERR_HIP;
+  if (launch() != hipSuccess) return fail();
   if (timing) {
-    if (hipEventRecord(rec.stop, stream) != hipSuccess) return ATTN_SINK_ERR_HIP;
+    if (hipEventRecord(rec.stop, stream) != hipSuccess) return fail();
     std::lock_guard<std::mutex> lk(g_mu);
     g_records.push_back(rec);
   }

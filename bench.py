@@ -108,10 +108,16 @@ def cpu_baseline(inp: dict, workload, pairs: int, budget_s: float = 12.0, gpu_ou
     `budget_s` seconds have been spent; report the algorithmic rate of that sample.
     If GPU outputs are given, also report their normwise error on the sample."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
 
     import oracle
 
+    # The oracle's threads: one per core this process may run on, at most the host
+    # share the GPU's jobs are given (OMP_NUM_THREADS where it is set).
+    threads = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        threads = max(1, min(threads, int(os.environ["OMP_NUM_THREADS"])))
+    limiter = threadpool_limits(limits=threads)
     group = workload.num_heads_q // workload.num_heads_kv
     done, t_total, errs = 0, 0.0, {}
     for g in range(workload.num_heads_kv):
@@ -135,12 +141,13 @@ def cpu_baseline(inp: dict, workload, pairs: int, budget_s: float = 12.0, gpu_ou
                 errs[name] = max(errs.get(name, 0.0), e)
         if t_total >= budget_s:
             break
+    limiter.restore_original_limits()
     d = workload.head_dim
     flop = pairs * group * done * 4 * d + pairs * group * done * 10 * d
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return dict(value=round(flop / t_total / 1e12, 6), unit="TFLOP/s", cores=int(threads), kind="oracle",
                 sample=f"{workload.name}: kv groups 0..{done - 1} ({done * group} of {workload.num_heads_q} query "
-                       f"heads), forward+backward, float64 numpy, {t_total:.1f} s"), errs
+                       f"heads), forward+backward, float64 numpy with {threads} BLAS threads, {t_total:.1f} s",
+                affinity_cores=len(os.sched_getaffinity(0))), errs
 
 
 def decode_bench(als, torch, dev, steps: int, warmup: int) -> dict:
@@ -209,6 +216,135 @@ def decode_bench(als, torch, dev, steps: int, warmup: int) -> dict:
     return res
 
 
+class Step:
+    """One fwd+bwd step of a workload layer on the device: inputs, outputs and the
+    backward workspace allocated once, outside any timed region."""
+
+    def __init__(self, als, torch, dev, w, layer):
+        from workloads import make_inputs
+
+        self.als, self.w = als, w
+        inp = make_inputs(w, layer=layer)
+        self.inp = inp
+        d = {k: inp[k].to(dev).contiguous() for k in ("q", "k", "v", "dout", "sinks", "cu_seqlens")}
+        self.d = d
+        cu = d["cu_seqlens"]
+        self.mx, self.scale = inp["max_seqlen"], inp["softmax_scale"]
+        self.causal, self.window = inp["causal"], inp["window"]
+        shape = als.make_shape(d["q"], d["k"], cu, cu, self.mx, self.mx, self.scale, self.causal, self.window)
+        self.ws = torch.empty(max(als.bwd_workspace_bytes(shape), 1), dtype=torch.uint8, device=dev)
+        self.o = torch.empty_like(d["q"])
+        self.lse = torch.empty(w.num_heads_q, w.total, dtype=torch.float32, device=dev)
+        self.dq, self.dk, self.dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
+        self.dsk = torch.empty_like(d["sinks"])
+        self.pairs = count_pairs(w.seqlens, self.causal, self.window)
+
+    def __call__(self):
+        d, cu, a = self.d, self.d["cu_seqlens"], self.als
+        a.fwd(d["q"], d["k"], d["v"], d["sinks"], cu, cu, self.mx, self.mx, self.scale, self.causal, self.window,
+              out=self.o, lse=self.lse)
+        a.bwd(d["q"], d["k"], d["v"], d["sinks"], self.o, self.lse, d["dout"], cu, cu, self.mx, self.mx, self.scale,
+              self.causal, self.window, workspace=self.ws, dq=self.dq, dk=self.dk, dv=self.dv, dsinks=self.dsk)
+
+    def host_outputs(self):
+        import numpy as np
+        return {k: t.float().cpu().numpy().astype(np.float64) for k, t in
+                dict(o=self.o, lse=self.lse, dq=self.dq, dk=self.dk, dv=self.dv, dsinks=self.dsk).items()}
+
+
+def kernel_events(als, torch, step, n):
+    """Average ms per launch of each library kernel over n steps (HIP events that the
+    library records on the launch stream), and the wall time per step."""
+    als.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern = als.timing_read()
+    als.timing_enable(False)
+    return {k: v[1] / v[0] for k, v in kern.items()}, (t1 - t0) * 1e3 / n
+
+
+def figures(w, step, per, workload_name):
+    """Forward / backward figures and the dominant kernel's roofline from per-launch
+    kernel durations (ms).  Algorithmic work: 4d FLOP forward and 10d backward per
+    visible (query, key) pair and query head; per kernel, the forward runs 2 GEMMs
+    (4d), the dQ kernel 3 (S, dP, dQ: 6d) and the dK/dV kernel 4 (S, dP, dV, dK: 8d).
+    Algorithmic bytes: each operand moved once."""
+    hd, hq, hkv, t_tok = w.head_dim, w.num_heads_q, w.num_heads_kv, w.total
+    pairs = step.pairs
+    fwd_flop, bwd_flop = 4 * hd * pairs * hq, 10 * hd * pairs * hq
+    elem = 2 if w.dtype == "bf16" else 4
+    mfma_peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    qb, kb = t_tok * hq * hd * elem, t_tok * hkv * hd * elem  # one [T, Hq, d] / [T, Hkv, d] tensor
+    rows = t_tok * hq * 4                                       # one fp32 value per row and head
+    kern_bytes = {
+        "attn_sink_fwd_kernel": qb + 2 * kb + qb + rows,                    # Q, K, V -> O, LSE
+        "attn_sink_bwd_dq_kernel": 3 * qb + 2 * kb + rows + qb + 2 * rows,  # Q, O, dO, K, V, LSE -> dQ, rows
+        "attn_sink_bwd_dkdv_kernel": 2 * qb + 2 * kb + 2 * rows + 2 * kb,   # Q, dO, K, V, rows -> dK, dV
+        "attn_sink_bwd_finish_kernel": 2 * kb,
+    }
+    gemm_d = {"attn_sink_fwd_kernel": 4, "attn_sink_bwd_dq_kernel": 6, "attn_sink_bwd_dkdv_kernel": 8}
+    fwd_ms = per.get("attn_sink_fwd_kernel", float("nan"))
+    bwd_ms = sum(v for k, v in per.items() if k != "attn_sink_fwd_kernel")
+    fwd_bytes = kern_bytes["attn_sink_fwd_kernel"]
+    bwd_bytes = 3 * qb + 2 * kb + rows + qb + 2 * kb + rows  # Q K V O dO LSE -> dQ dK dV, plus D
+
+    def leg(flop, byts, ms):
+        tf = flop / (ms * 1e-3) / 1e12
+        gbs = byts / (ms * 1e-3) / 1e9
+        return {"ms": round(ms, 5), "tflops": round(tf, 3), "frac_of_peak": round(tf / mfma_peak, 4),
+                "algorithmic_gbs": round(gbs, 1), "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+
+    dom = max(per, key=per.get)
+    ridge = mfma_peak * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP per byte where the two peaks meet
+    flop = gemm_d.get(dom, 0) * hd * pairs * hq
+    byts = kern_bytes.get(dom, 0)
+    if flop > 0 and flop / max(byts, 1) >= ridge:
+        work, unit, bound, peak = flop / 1e12, "TFLOP/s", "mfma", mfma_peak
+    else:
+        work, unit, bound, peak = byts / 1e9, "GB/s", "hbm", PEAK_HBM_GBS
+    achieved = work / (per[dom] * 1e-3)
+    roofline = dict(bound=bound, achieved=round(achieved, 3), peak=peak, unit=unit, frac=round(achieved / peak, 4),
+                    traffic=read_traffic(workload_name, dom), kernel=dom, launch_ms=round(per[dom], 5),
+                    flop_per_byte=round(flop / max(byts, 1), 1))
+    return {"fwd": leg(fwd_flop, fwd_bytes, fwd_ms), "bwd": leg(bwd_flop, bwd_bytes, bwd_ms),
+            "fwd_bwd_tflops": round((fwd_flop + bwd_flop) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 3),
+            "kernels_ms_per_launch": {k: round(v, 5) for k, v in per.items()},
+            "roofline": roofline}, fwd_flop, bwd_flop
+
+
+# The other workload layers, measured in the same run (their parity is the GPU tests'):
+# (name, layer) in the order they are reported.
+OTHER_CONFIGS = [("tiny", 0), ("window_16k", 0), ("varlen", 0), ("varlen", 1), ("long_20k", 0), ("d128_4k", 0)]
+
+
+def config_bench(als, torch, dev, steps: int, warmup: int) -> dict:
+    """Per-workload fwd / bwd figures from the library's per-kernel events (a warm-up,
+    then `steps` steps with events); each layer's buffers are freed before the next."""
+    from workloads import WORKLOADS
+
+    out = {}
+    for name, layer in OTHER_CONFIGS:
+        w = WORKLOADS[name]
+        key = f"{name}:{layer}" if len(w.layers) > 1 else name
+        step = Step(als, torch, dev, w, layer)
+        n = steps if step.pairs * w.num_heads_q < 5e10 else max(3, steps // 4)  # long layers: fewer steps
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        per, _ = kernel_events(als, torch, step, n)
+        fig, _, _ = figures(w, step, per, key.replace(":", "_layer"))
+        fig.update(steps=n, dtype=w.dtype, seqlens=len(w.seqlens), total=w.total, heads=[w.num_heads_q, w.num_heads_kv],
+                   head_dim=w.head_dim, window=int(step.window), causal=bool(step.causal))
+        out[key] = fig
+        del step
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,6 +359,7 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this size first (for counter calibration)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decoding-step leg")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other workload layers")
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="extra steps, each after rewriting a 512 MiB buffer (L2 and MALL flushed), timed apart")
     args = ap.parse_args()
@@ -232,25 +369,16 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import attention_learnable_sinks_amd as als
-    from workloads import WORKLOADS, make_inputs
+    from workloads import WORKLOADS
 
     als.load()
     dev = torch.device("cuda:0")
     w = WORKLOADS[args.workload]
-    inp = make_inputs(w, layer=args.layer)
-    d = {k: inp[k].to(dev).contiguous() for k in ("q", "k", "v", "dout", "sinks", "cu_seqlens")}
-    cu = d["cu_seqlens"]
-    mx, scale, causal, window = inp["max_seqlen"], inp["softmax_scale"], inp["causal"], inp["window"]
-    shape = als.make_shape(d["q"], d["k"], cu, cu, mx, mx, scale, causal, window)
-    ws = torch.empty(als.bwd_workspace_bytes(shape), dtype=torch.uint8, device=dev)
-    o = torch.empty_like(d["q"])
-    lse = torch.empty(w.num_heads_q, w.total, dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
-    dsk = torch.empty_like(d["sinks"])
+    step = Step(als, torch, dev, w, args.layer)
+    causal, window, scale = step.causal, step.window, step.scale
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 4
@@ -260,11 +388,6 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def step():
-        als.fwd(d["q"], d["k"], d["v"], d["sinks"], cu, cu, mx, mx, scale, causal, window, out=o, lse=lse)
-        als.bwd(d["q"], d["k"], d["v"], d["sinks"], o, lse, d["dout"], cu, cu, mx, mx, scale, causal, window,
-                workspace=ws, dq=dq, dk=dk, dv=dv, dsinks=dsk)
-
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -273,15 +396,7 @@ def main():
     # markers per step, so `value` comes from the next, uninstrumented pass.  At least
     # 40 steps, so the GPU has settled before that pass even with a short warm-up.
     n_ev = max(args.steps, 40)
-    als.timing_enable(True)
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    for _ in range(n_ev):
-        step()
-    torch.cuda.synchronize()
-    t3 = time.perf_counter()
-    kern = als.timing_read()
-    als.timing_enable(False)
+    per, ms_ev = kernel_events(als, torch, step, n_ev)
     # The K timed steps, uninstrumented: `value` and ms_per_step.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -289,6 +404,7 @@ def main():
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    host = None if args.no_cpu else step.host_outputs()
 
     # Cold-cache steps: a 512 MiB write between steps evicts L2 and the MALL; only the
     # library's kernels are timed (HIP events around each launch).
@@ -308,63 +424,30 @@ def main():
                 "bwd_ms": round(sum(v for k, v in per_c.items() if k != "attn_sink_fwd_kernel"), 5),
                 "steps": args.cold_steps}
 
-    pairs = count_pairs(w.seqlens, causal, window)
-    hd = w.head_dim
-    fwd_flop = 4 * hd * pairs * w.num_heads_q
-    bwd_flop = 10 * hd * pairs * w.num_heads_q
+    fig, fwd_flop, bwd_flop = figures(w, step, per, args.workload)
     ms = (t1 - t0) * 1e3 / args.steps
     value = (fwd_flop + bwd_flop) / (ms * 1e-3) / 1e12
-
-    per = {k: v[1] / v[0] for k, v in kern.items()}  # average ms per launch
-    fwd_ms = per.get("attn_sink_fwd_kernel", float("nan"))
-    bwd_ms = sum(v for k, v in per.items() if k != "attn_sink_fwd_kernel")
-    # Dominant kernel by time and its algorithmic work per launch: the forward does
-    # 2 GEMMs (4d FLOP per visible pair and query head), the dQ kernel 3 (S, dP, dQ:
-    # 6d) and the dK/dV kernel 4 (S, dP, dV, dK: 8d); the small kernels move bytes.
-    dom = max(per, key=per.get)
-    elem = 2 if w.dtype == "bf16" else 4
-    t_tok, hq, hkv = w.total, w.num_heads_q, w.num_heads_kv
-    mfma_peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
-    # Algorithmic bytes per launch (each operand moved once) and FLOP per launch.
-    qb, kb = t_tok * hq * hd * elem, t_tok * hkv * hd * elem  # one [T, Hq, d] / [T, Hkv, d] tensor
-    rows = t_tok * hq * 4                                       # one fp32 value per row and head
-    kern_bytes = {
-        "attn_sink_fwd_kernel": qb + 2 * kb + qb + rows,                 # Q, K, V -> O, LSE
-        "attn_sink_bwd_dq_kernel": 3 * qb + 2 * kb + rows + qb + 2 * rows,  # Q, O, dO, K, V, LSE -> dQ, lse*log2e, -D
-        "attn_sink_bwd_dkdv_kernel": 2 * qb + 2 * kb + 2 * rows + 2 * kb,  # Q, dO, K, V, rows -> dK, dV
-        "attn_sink_bwd_finish_kernel": 2 * kb,
-    }
-    gemm_d = {"attn_sink_fwd_kernel": 4, "attn_sink_bwd_dq_kernel": 6, "attn_sink_bwd_dkdv_kernel": 8}
-    ridge = mfma_peak * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP per byte where the two peaks meet
-    flop = gemm_d.get(dom, 0) * hd * pairs * hq
-    byts = kern_bytes.get(dom, 0)
-    if flop > 0 and flop / max(byts, 1) >= ridge:
-        work, unit, bound, peak = flop / 1e12, "TFLOP/s", "mfma", mfma_peak
-    else:
-        work, unit, bound, peak = byts / 1e9, "GB/s", "hbm", PEAK_HBM_GBS
-    achieved = work / (per[dom] * 1e-3)
-    roofline = dict(bound=bound, achieved=round(achieved, 3), peak=peak, unit=unit, frac=round(achieved / peak, 4),
-                    traffic=read_traffic(args.workload, dom), kernel=dom, launch_ms=round(per[dom], 5),
-                    flop_per_byte=round(flop / max(byts, 1), 1))
+    roofline = fig["roofline"]
+    dom = roofline["kernel"]
     # The same against the clock the kernel actually ran at (CUs x 4096 bf16 FLOP per clock x
     # the core clock from the committed counter run, an upper bound, so this fraction is a
     # lower bound).
-    sclk = read_sclk(args.workload, dom) if bound == "mfma" and w.dtype == "bf16" else None
+    sclk = read_sclk(args.workload, dom) if roofline["bound"] == "mfma" and w.dtype == "bf16" else None
     if sclk is not None:
         cus = torch.cuda.get_device_properties(dev).multi_processor_count
         adj = cus * 4096 * sclk * 1e9 / 1e12
         roofline.update(sclk_ghz=sclk, clock_adjusted_peak=round(adj, 1),
-                        frac_of_clock_adjusted_peak=round(achieved / adj, 4))
-    fwd_bytes = kern_bytes["attn_sink_fwd_kernel"]
-    bwd_bytes = 3 * qb + 2 * kb + rows + qb + 2 * kb + rows  # Q K V O dO LSE -> dQ dK dV, plus D (37,376 B per token at 64/8 heads)
+                        frac_of_clock_adjusted_peak=round(roofline["achieved"] / adj, 4))
+    inp = step.inp
+    del step
+    torch.cuda.empty_cache()
 
+    configs = None if args.no_configs else config_bench(als, torch, dev, max(args.steps, 10), max(args.warmup, 5))
     dec = None if args.no_decode else decode_bench(als, torch, dev, max(args.steps, 10), max(args.warmup, 2))
 
     cpu, errs = None, {}
     if not args.no_cpu:
-        host = {k: t.float().cpu().numpy().astype(np.float64) for k, t in
-                dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv, dsinks=dsk).items()}
-        cpu, errs = cpu_baseline(inp, w, pairs, args.cpu_budget, host)
+        cpu, errs = cpu_baseline(inp, w, count_pairs(w.seqlens, causal, window), args.cpu_budget, host)
 
     out = {
         "metric": "attention fwd+bwd TFLOP/s and % bf16 MFMA peak, GPT-OSS-20B shape",
@@ -374,7 +457,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
-        "ms_per_step_with_kernel_events": round((t3 - t2) * 1e3 / n_ev, 5),
+        "ms_per_step_with_kernel_events": round(ms_ev, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -384,17 +467,12 @@ def main():
                    "num_heads_q": w.num_heads_q, "num_heads_kv": w.num_heads_kv, "head_dim": w.head_dim,
                    "causal": bool(causal), "window": int(window), "softmax_scale": scale},
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "fwd": {"ms": round(fwd_ms, 5), "tflops": round(fwd_flop / (fwd_ms * 1e-3) / 1e12, 3),
-                "frac_of_peak": round(fwd_flop / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                "algorithmic_gbs": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9, 1),
-                "frac_of_hbm": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-        "bwd": {"ms": round(bwd_ms, 5), "tflops": round(bwd_flop / (bwd_ms * 1e-3) / 1e12, 3),
-                "frac_of_peak": round(bwd_flop / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                "algorithmic_gbs": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9, 1),
-                "frac_of_hbm": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "fwd": fig["fwd"],
+        "bwd": fig["bwd"],
         "cold_cache": cold,
+        "configs": configs,
         "decode": dec,
-        "kernels_ms_per_launch": {k: round(v, 5) for k, v in per.items()},
+        "kernels_ms_per_launch": fig["kernels_ms_per_launch"],
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity_on_cpu_sample": {k: float(f"{v:.3e}") for k, v in errs.items()} or None,

@@ -44,8 +44,11 @@
  * Outputs (o, lse, dq, dk, dv, dsinks) are overwritten, not accumulated.
  *
  * Errors: every argument check runs on the host before anything is enqueued, so
- * on any non-OK status nothing has been enqueued.  ATTN_SINK_ERR_HIP reports a
- * launch error taken from the HIP runtime.  Faults inside a kernel are
+ * a status of ATTN_SINK_ERR_INVALID_ARG, _UNSUPPORTED or _WORKSPACE means nothing
+ * has been enqueued.  ATTN_SINK_ERR_HIP reports a launch error taken from the HIP
+ * runtime; an entry point that launches several kernels (attn_sink_bwd,
+ * attn_sink_fwd_decode) may by then have enqueued the kernels before the one that
+ * failed, and its outputs are then undefined.  Faults inside a kernel are
  * asynchronous and surface at the caller's next synchronisation.  The kernels
  * clamp cu_seqlens entries to [0, total] before use, so a malformed cu_seqlens
  * gives wrong numbers but no out-of-bounds access; sequences longer than
