@@ -45,10 +45,13 @@ struct DqCfg {
   static constexpr int BN = 64;   // keys per tile
   static constexpr int THREADS = 256;
   static constexpr int TILE = tile_elems_d<T, D>(BN);
+  // Workgroups resident per compute unit the register budget is set for: three at
+  // bf16 d = 64 (168 registers), two at bf16 d = 128; fp32 is left to the compiler.
+  static constexpr int MIN_WG = sizeof(T) == 2 ? (D == 64 ? 3 : 2) : 1;
 };
 
 template <typename T, int D, bool PKH>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, (DqCfg<T, D>::MIN_WG)) void bwd_dq_kernel(BwdArgs a) {
   using C = DqCfg<T, D>;
   using M = Mfma<T>;
   constexpr int E = M::E, KS = M::KS;
@@ -144,40 +147,20 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const float dd = halves_sum(dpart);  // D of the lane's row (0 past the sequence)
   const float lse2 = lse * kLog2e;
   const float sl2 = f.scale * kLog2e;
-  // Row statistics for the dK/dV kernel, and this workgroup's share of
-  // dS_h = -sum_i P_sink_i D_i (fixed-order reduction: lanes, then wavefronts).
-  {
-    const bool writer = qok && h == 0;
-    if (writer) {
-      a.rowstat[(size_t)(2 * head) * f.total_q + sq.start + qi] = lse2;
-      a.rowstat[(size_t)(2 * head + 1) * f.total_q + sq.start + qi] = -dd;
-    }
-    const float sink = f.sinks[head];
-    const float ps = (writer && lse > -INFINITY && sink > -INFINITY) ? fast_exp2((sink - lse) * kLog2e) : 0.f;
-    float contrib = -ps * dd;
-    if constexpr (PKH) {
-      if (h == 0) red[32 * w + c] = contrib;  // by row; summed per head below
-    } else {
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) contrib += __shfl_xor(contrib, m);
-      if (lane == 0) red[w] = contrib;
-    }
+  // Row statistics for the dK/dV kernel: -lse * log2(e) (the seed of its score
+  // accumulator) and -D (the seed of its dP accumulator).
+  const bool writer = qok && h == 0;
+  if (writer) {
+    a.rowstat[(size_t)(2 * head) * f.total_q + sq.start + qi] = -lse2;
+    a.rowstat[(size_t)(2 * head + 1) * f.total_q + sq.start + qi] = -dd;
   }
+  // This lane's float32 sum of dS_ij = P_ij (dP_ij - D_i) over its keys (see the epilogue).
+  float dsum = 0.f;
   f32x16 neg_dd;  // -D of the lane's row in every register
 #pragma unroll
   for (int r = 0; r < 16; ++r) neg_dd[r] = -dd;
   vmem_drain();
   __syncthreads();
-  if constexpr (PKH) {
-    // head g*G + tid: its rows tid, tid + G, ... in order
-    if (tid < G) {
-      float acc = 0.f;
-      for (int r = tid; r < C::BM; r += G) acc += red[r];
-      dsink_slot[(size_t)tid * a.pre_blocks] = acc;
-    }
-  } else {
-    if (tid == 0) *dsink_slot = (red[0] + red[1]) + (red[2] + red[3]);
-  }
 
   // One tile: S^T, dP^T, P^T, dS^T, dQ^T += K^T dS^T; FULL tiles need no mask.
   auto body = [&](const T* Ks, const T* Vs, int kbase, auto full_tag) {
@@ -206,6 +189,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
       }
     }
     __builtin_amdgcn_s_setprio(0);
+    float tsum[2];  // the tile's row sums of dS^T, one chain per 32 keys
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -214,7 +198,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
         if constexpr (!FULL)  // key kbase + 4h + (32 mt + 8 (r/4) + r%4)
           pv = in_span(kbase + 4 * h + 32 * mt + 8 * (r / 4) + r % 4, row_keys) ? pv : 0.f;
         st[mt][r] = pv * (sizeof(T) == 2 ? dpt[mt][r] : dpt[mt][r] - dd);  // dS^T = P^T (dP^T - D)
+        tsum[mt] = r == 0 ? st[mt][r] : tsum[mt] + st[mt][r];
       }
+    dsum += tsum[0] + tsum[1];
     // dQ^T[d x q] += K^T[d x keys] . dS^T[keys x q]
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -259,6 +245,42 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   for (; kt < wf_lo; ++kt) step(kt, std::false_type{});
   for (; kt < wf_hi; ++kt) step(kt, std::true_type{});
   for (; kt < kt_end; ++kt) step(kt, std::false_type{});
+
+  // This workgroup's share of dS_h = -sum_i P_sink_i D_i.  D_i = sum_j P_ij dP_ij
+  // is taken from the float32 P and dP of the loop, not from <dO_i, O_i> with O
+  // rounded to the element type: a head whose dS_h is a near cancellation of its
+  // rows' terms (large sinks over long rows) would otherwise carry that rounding
+  // (about 2^-9 of each D_i) into a result many times smaller than the terms.
+  // The loop summed dS_ij = P_ij (dP_ij - D'_i), D' = <dO_i, O_i>, so
+  //   D_i = sum_j dS_ij + D'_i sum_j P_ij = sum_j dS_ij + D'_i (1 - P_sink_i).
+  // Fixed-order reduction: lanes, then wavefronts (packed tiles: rows per head).
+  {
+    // (P_sink_i and D'_i are formed again here rather than held through the loop.)
+    const float lse_e = qok ? f.lse[(size_t)head * f.total_q + sq.start + qi] : 0.f;
+    const float sink = f.sinks[head];
+    const bool wr = qok && h == 0;
+    const float ps = (wr && lse_e > -INFINITY && sink > -INFINITY) ? fast_exp2((sink - lse_e) * kLog2e) : 0.f;
+    const float d_row = halves_sum(dsum) - neg_dd[0] * (1.f - ps);
+    float contrib = wr ? -ps * d_row : 0.f;
+    if constexpr (PKH) {
+      if (h == 0) red[32 * w + c] = contrib;  // by row; summed per head below
+    } else {
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) contrib += __shfl_xor(contrib, m);
+      if (lane == 0) red[w] = contrib;
+    }
+    __syncthreads();
+    if constexpr (PKH) {
+      // head g*G + tid: its rows tid, tid + G, ... in order
+      if (tid < G) {
+        float acc = 0.f;
+        for (int r = tid; r < C::BM; r += G) acc += red[r];
+        dsink_slot[(size_t)tid * a.pre_blocks] = acc;
+      }
+    } else {
+      if (tid == 0) *dsink_slot = (red[0] + red[1]) + (red[2] + red[3]);
+    }
+  }
 
   if (qok) {
     T* dst = static_cast<T*>(a.dq) + (size_t)(sq.start + qi) * q_row + head * D;
@@ -305,7 +327,7 @@ __global__ __launch_bounds__((DkvCfg<T, D>::THREADS), (sizeof(T) == 2 && D == 64
   // add one row-statistics load), for the waits in step().
   constexpr int kStageVm = 2 * QLoader::N;
   __shared__ __attribute__((aligned(16))) T smem[NB * 2 * C::TILE];  // [buf][Q, dO]
-  __shared__ __attribute__((aligned(16))) float lse2_s[NB][C::BMB];
+  __shared__ __attribute__((aligned(16))) float nlse_s[NB][C::BMB];  // -lse * log2(e) of the tile's rows
   __shared__ __attribute__((aligned(16))) float dd_s[NB][C::BMB];
 
   const XcdSlot slot = xcd_slot(blockIdx.x, f.hkv, a.splits);
@@ -372,6 +394,7 @@ __global__ __launch_bounds__((DkvCfg<T, D>::THREADS), (sizeof(T) == 2 && D == 64
         vf[s] = global_frag<T>(vsrc + KS * s + E * h, kok);
       }
     }
+
     f32x16 dkt[D / 32], dvt[D / 32];  // dK^T, dV^T: [D x 32 keys]
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
@@ -399,7 +422,7 @@ __global__ __launch_bounds__((DkvCfg<T, D>::THREADS), (sizeof(T) == 2 && D == 64
       dold.issue(qt * C::BMB, smem + buf * 2 * C::TILE + C::TILE);
       // The row statistics go straight to LDS as well (rows past the sequence read
       // as 0), so no load in the loop writes a register the loop has to wait for.
-      if (w == 0) lld.issue(qt * C::BMB, lse2_s[buf], lane);
+      if (w == 0) lld.issue(qt * C::BMB, nlse_s[buf], lane);
       if (w == 1) dld.issue(qt * C::BMB, dd_s[buf], lane);
     };
     auto commit = [&](int buf) __device__ {
@@ -427,18 +450,15 @@ __global__ __launch_bounds__((DkvCfg<T, D>::THREADS), (sizeof(T) == 2 && D == 64
 #pragma unroll
       for (int mq = 0; mq < 2; ++mq) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          pt[mq][r] = 0.f;
-          dst[mq][r] = 0.f;
-        }
-        f32x16 seed;  // bf16: -D of each register's query row (dd_s holds -D); dP then ends at dP - D
-        if constexpr (sizeof(T) == 2) {
+        for (int r = 0; r < 16; ++r) pt[mq][r] = 0.f;
+        // -D of each register's query row (dd_s holds -D): the seed of the dP
+        // accumulator, which then ends at dP - D.
+        f32x16 seed;
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dd_s[buf][32 * mq + crow(4 * r4, h)]);
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dd_s[buf][32 * mq + crow(4 * r4, h)]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) seed[4 * r4 + e] = d4[e];
-          }
+          for (int e = 0; e < 4; ++e) seed[4 * r4 + e] = d4[e];
         }
         // All operands of this block's 8 MFMAs are read first; the scheduling barrier
         // keeps the reads from being sunk next to their MFMAs (which would expose the
@@ -453,10 +473,7 @@ __global__ __launch_bounds__((DkvCfg<T, D>::THREADS), (sizeof(T) == 2 && D == 64
 #pragma unroll
         for (int s = 0; s < D / KS; ++s) {
           pt[mq] = M::mma(qa[s], kf[s], pt[mq]);
-          if constexpr (sizeof(T) == 2)
-            dst[mq] = s == 0 ? mma_seeded(da[s], vf[s], seed) : M::mma(da[s], vf[s], dst[mq]);
-          else
-            dst[mq] = M::mma(da[s], vf[s], dst[mq]);
+          dst[mq] = s == 0 ? mma_first<T>(da[s], vf[s], seed) : M::mma(da[s], vf[s], dst[mq]);
         }
       }
 #pragma unroll
@@ -464,19 +481,17 @@ __global__ __launch_bounds__((DkvCfg<T, D>::THREADS), (sizeof(T) == 2 && D == 64
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int ql = 32 * mq + crow(4 * r4, h);  // 4 consecutive query rows
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2_s[buf][ql]);
-          f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
-          if constexpr (sizeof(T) != 2) d4 = *reinterpret_cast<const f32x4*>(&dd_s[buf][ql]);
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&nlse_s[buf][ql]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * r4 + e;
-            float pv = fast_exp2(fmaf(pt[mq][r], sl2, -l4[e]));
+            float pv = fast_exp2(fmaf(pt[mq][r], sl2, l4[e]));  // nlse_s holds -lse * log2(e)
             if constexpr (!FULL) {
               // query qbase + 4h + (32 mq + 8 r4 + e), a constant per element
               pv = in_span(qbase + 4 * h + 32 * mq + 8 * r4 + e, key_rows) ? pv : 0.f;
             }
             pt[mq][r] = pv;
-            dst[mq][r] = pv * (sizeof(T) == 2 ? dst[mq][r] : dst[mq][r] + d4[e]);  // dS = P (dP - D); d4 = -D
+            dst[mq][r] = pv * dst[mq][r];  // dS = P (dP - D)
           }
         }
       // dV^T[d x keys] += dO^T[d x q] P[q x keys];  dK^T += Q^T dS

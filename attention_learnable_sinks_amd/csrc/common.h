@@ -216,24 +216,12 @@ __device__ inline typename Mfma<T>::Frag frag_col(const FragAddr<T>& fa, const T
   return fa.col(tile + (md / 2) * tile_elems<T>(ROWS), md % 2, s);
 }
 
-// acc += A B (bf16, 32x32x16) with the accumulator held in AGPRs.  Accumulators
-// that the vector ALUs never touch inside a loop (O, dQ, dK, dV) live there so the
-// MFMA's accumulator traffic does not compete with the VALU work of the other
-// wavefronts for the VGPR file.  Written as inline asm because the compiler,
-// told to keep the softmax tiles in VGPRs, would otherwise copy the accumulator
-// back and forth.  Hazards the compiler does not see through the asm: a VALU write
-// of A, B or the accumulator needs 2 wait states before the MFMA reads it (the
-// leading s_nop); the MFMA result needs agpr_fence() before any VALU reads it.
-// Back-to-back MFMAs on the same accumulator need none.
-__device__ inline void mma_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
 // d = A B + c (bf16, 32x32x16) with c in registers distinct from d: the first
 // step of an accumulation that starts from a non-zero seed kept elsewhere (the
 // compiler would first copy the seed into d).  The leading s_nop covers a VALU
 // write of A, B or c just before.  MFMAs that go on accumulating into d need no
 // wait states; a VALU read of d must come after a later compiler-emitted MFMA
-// (or after agpr_fence-like padding).  Not volatile: a volatile asm would be a
+// on d (the compiler does not see this one's latency).  Not volatile: a volatile asm would be a
 // scheduling boundary and pin the LDS operand reads around it.
 __device__ inline f32x16 mma_seeded(bf16x8 a, bf16x8 b, const f32x16& c) {
   f32x16 d;
@@ -241,9 +229,15 @@ __device__ inline f32x16 mma_seeded(bf16x8 a, bf16x8 b, const f32x16& c) {
   return d;
 }
 
-// 16 wait states: covers an MFMA result read by the vector ALUs (12 needed).
-__device__ inline void agpr_fence(f32x16& a0, f32x16& a1) {
-  asm volatile("s_nop 7\n\ts_nop 7" : "+a"(a0), "+a"(a1));
+// d = A B + c with the seed c kept in its own registers (first step of a seeded
+// accumulation): bf16 through mma_seeded, fp32 through the builtin.
+template <typename T>
+__device__ inline f32x16 mma_first(typename Mfma<T>::Frag a, typename Mfma<T>::Frag b, const f32x16& c) {
+  if constexpr (Mfma<T>::E == 8) {
+    return mma_seeded(a, b, c);
+  } else {
+    return Mfma<T>::mma(a, b, c);
+  }
 }
 
 // Pack flat registers [E*s, E*s + E) of two stacked C tiles into an operand.

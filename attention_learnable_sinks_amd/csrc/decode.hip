@@ -171,13 +171,22 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[mt][r] = fast_exp2(fmaf(st[mt][r], sl2, neg_m));
+    // The normaliser sums the float32 P before it is rounded into operands, as the
+    // training forward does, so the two paths differ only in summation order.
+    float tsum = 0.f;
 #pragma unroll
     for (int s = 0; s < NP; ++s) {
+      if constexpr (sizeof(T) == 2) {
+        const int r0 = 8 * (s % 2);
+        const f32x16& x = st[s / 2];
+        tsum += ((x[r0] + x[r0 + 1]) + (x[r0 + 2] + x[r0 + 3])) + ((x[r0 + 4] + x[r0 + 5]) + (x[r0 + 6] + x[r0 + 7]));
+      }
       const Frag pf = pack_frag<T>(st, s);
-      l_run = frag_sum<T>(pf, l_run);  // the sum of the rounded P that multiplies V
+      if constexpr (sizeof(T) != 2) tsum = frag_sum<T>(pf, tsum);
 #pragma unroll
       for (int md = 0; md < D / 32; ++md) oacc[md] = M::mma(frag_col<T, kDecBN>(fa, Vs, md, s), pf, oacc[md]);
     }
+    l_run += tsum;
   };
 
   // Each wavefront moves its own tiles and waits only for its own loads (no

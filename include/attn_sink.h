@@ -144,6 +144,14 @@ size_t attn_sink_bwd_workspace_bytes(const attn_sink_shape* shape);
  * softmax over the score row with the sink column appended).
  * o and lse must be the forward's outputs for the same inputs.  Writes dq (dtype,
  * layout of q), dk/dv (dtype, layout of k) and dsinks (float32, [Hq]).
+ * dsinks_h = -sum_i P_sink_i D_i is formed with D_i = sum_j P_ij dP_ij from the
+ * float32 probabilities the call recomputes, as
+ *   -sum_i P_sink_i (sum_j dS_ij + D'_i (1 - P_sink_i)),  D'_i = <dout_i, o_i>,
+ * which is exact when the call sees every key of each row (sum_j P_ij =
+ * 1 - P_sink_i).  D'_i alone would carry the rounding of o into a sum whose terms
+ * can cancel to a small fraction of their size.  A call over a shard of the keys
+ * returns its shard's part plus the key-free term -sum_i P_sink_i D'_i
+ * (1 - P_sink_i) (see attn_sink_merge for combining shards).
  * workspace: device memory of at least attn_sink_bwd_workspace_bytes(shape)
  * bytes, 256-byte aligned, owned by the caller, contents need not be initialised
  * and are garbage afterwards.  No atomics are used: dq is produced by one
@@ -178,8 +186,10 @@ attn_sink_status attn_sink_bwd(const attn_sink_shape* shape,
  * (dtype), lse [Hq, total_q] float32.  Outputs must not alias the inputs.
  * The backward of the sharded attention needs no merge kernel: calling
  * attn_sink_bwd per shard with the merged o and lse gives that shard's dk, dv and
- * its share of dq (summed over the shards); dsinks depends only on the merged o,
- * lse and dout, so every shard's call returns the same dsinks (take one).
+ * its share of dq (summed over the shards).  Each such call's dsinks is its
+ * shard's part of the sink gradient plus a term that does not depend on the keys
+ * (see attn_sink_bwd), which a call with no keys (total_k = 0) returns alone:
+ * over n shards, dsinks = sum of the shard calls' dsinks - (n - 1) x that call's.
  * Errors: ATTN_SINK_ERR_UNSUPPORTED for dtype / head_dim; ATTN_SINK_ERR_INVALID_ARG
  * for num_heads_q < 1, total_q < 0, num_parts < 1 or a null pointer. */
 attn_sink_status attn_sink_merge(int dtype, int head_dim, int num_heads_q, int total_q, int num_parts,

@@ -74,3 +74,37 @@ def compare(gpu: dict, ref: dict, keys, tol: float, label: str = "") -> dict:
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, f"{label}: over tolerance {tol}: {bad}"
     return errs
+
+
+def sink_terms(inp: dict, ref: dict) -> np.ndarray:
+    """sum_i |P_sink_i D_i| per head, from the oracle's own O and LSE: the size of the
+    terms whose sum is dS_h (its condition scale: dS_h can cancel to a small fraction
+    of it, where float32 arithmetic on the terms leaves an error of a few units of
+    roundoff times this sum)."""
+    sinks = inp["sinks"].double().numpy()
+    dout = inp["dout"].double().numpy()
+    with np.errstate(invalid="ignore"):
+        ps = np.exp(sinks[:, None] - ref["lse"])                 # [Hq, T]
+        d = np.einsum("thc,thc->ht", dout, ref["o"])             # [Hq, T]
+        return np.nansum(np.abs(ps * d), axis=1)
+
+
+def compare_dsinks_per_head(gpu: dict, ref: dict, heads, tol: float, label: str = "", terms=None,
+                            roundoff: float = 0.0) -> np.ndarray:
+    """dS_h head by head (a head whose reference is small is not hidden behind the
+    largest one, as it is normwise): |dS_h - ref| <= tol |ref| + roundoff sum_i
+    |P_sink_i D_i|.  With roundoff = 0 (the default) this is the plain per-head
+    relative error |dS_h - ref| / |ref| <= tol."""
+    heads = list(heads)
+    g, r = gpu["dsinks"][heads], ref["dsinks"][heads]
+    assert np.all(np.isfinite(r)) and np.all(np.isfinite(g))
+    t = np.zeros(len(heads)) if terms is None else np.asarray(terms)[heads]
+    errs = np.abs(g - r) / np.maximum(np.abs(r), 1e-30)
+    bound = tol + roundoff * t / np.maximum(np.abs(r), 1e-30)
+    cond = t / np.maximum(np.abs(r), 1e-30)
+    print(f"[parity] {label} dS_h per head (rel. error, condition sum|terms|/|dS_h|): " +
+          " ".join(f"{h}:{e:.1e}" + (f"/{c:.0f}" if terms is not None else "") for h, e, c in zip(heads, errs, cond)),
+          flush=True)
+    bad = {int(h): float(e) for h, e, b in zip(heads, errs, bound) if not e <= b}
+    assert not bad, f"{label}: dS_h over tolerance {tol} for heads {bad}"
+    return errs

@@ -3,7 +3,8 @@ shard is attended with the sink switched off (attn_sink_fwd, S_h = -inf), and
 attn_sink_merge combines the partials, adding the sink once.  The merged output
 must equal the oracle's sink attention over all the keys; the backward, run per
 shard with the merged O and LSE, must give the full gradients (dq summed over the
-shards, dk / dv per shard, dsinks from any one shard).  The shards stand in for
+shards, dk / dv per shard, dsinks as the shards' sum less n - 1 times a call with
+no keys).  The shards stand in for
 devices: what crosses devices in a real run (the partials, dq, dsinks) is exactly
 what these tests combine."""
 
@@ -137,7 +138,10 @@ def test_sharded_causal_ring_equals_full_attention(gpu_lib):
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_sharded_backward_equals_full_gradients(gpu_lib, dtype):
     """Per-shard attn_sink_bwd with the merged o, lse: dq summed over the shards,
-    dk / dv from each shard, dsinks identical from every shard."""
+    dk / dv from each shard.  dsinks: each call returns its shard's part of
+    -sum_i P_sink_i sum_j P_ij dP_ij plus the key-independent term
+    -sum_i P_sink_i D_i (1 - P_sink_i) (D_i = <dO_i, O_i>), which a call with no keys
+    returns alone; so dS_h = sum over the shards - (shards - 1) x that call."""
     shards = 3
     inp = random_case([300, 77, 513], 8, 2, 64, dtype, seed=50, causal=False, scale=0.125)
     o, lse = _sharded_forward(gpu_lib, inp, shards)
@@ -154,9 +158,14 @@ def test_sharded_backward_equals_full_gradients(gpu_lib, dtype):
         dk_parts.append(dk_s.double().cpu())
         dv_parts.append(dv_s.double().cpu())
         ds.append(ds_s)
+    none = torch.zeros(0, inp["k"].shape[1], 64, dtype=q.dtype, device="cuda")
+    cu0 = torch.zeros_like(cuq)
+    ds_none = gpu_lib.bwd(q, none, none, sinks, o, lse, do, cuq, cu0, inp["max_seqlen"], 0, 0.125, False, 0)[3]
+    dsinks = sum(x.double() for x in ds) - (shards - 1) * ds_none.double()
+    full = gpu_lib.bwd(q, dev(inp["k"]), dev(inp["v"]), sinks, o, lse, do, cuq, cuq, inp["max_seqlen"],
+                       inp["max_seqlen"], 0.125, False, 0)[3]
     torch.cuda.synchronize()
-    for x in ds[1:]:
-        assert torch.equal(x, ds[0])  # the sink gradient depends only on the merged o, lse, dout
+    torch.testing.assert_close(dsinks.float(), full, rtol=1e-5, atol=1e-6)  # as one call over all keys
     # reassemble dk / dv in the packed order of the full key tensor
     cu = inp["cu_seqlens"].tolist()
     dk = torch.zeros(inp["k"].shape, dtype=torch.float64)
@@ -169,7 +178,7 @@ def test_sharded_backward_equals_full_gradients(gpu_lib, dtype):
             dv[cu[b] + lo:cu[b] + hi] = dv_parts[s][cuk[b]:cuk[b + 1]]
     ref = oracle.sink_attention_backward(inp["q"], inp["k"], inp["v"], inp["sinks"], inp["dout"],
                                          inp["cu_seqlens"], inp["cu_seqlens"], 0.125, False, 0)
-    got = dict(dq=dq.numpy(), dk=dk.numpy(), dv=dv.numpy(), dsinks=_np(ds[0]))
+    got = dict(dq=dq.numpy(), dk=dk.numpy(), dv=dv.numpy(), dsinks=_np(dsinks))
     compare(got, ref, ("dq", "dk", "dv", "dsinks"), TOL[dtype], f"sharded bwd {dtype}")
 
 

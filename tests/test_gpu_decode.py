@@ -89,16 +89,29 @@ def test_decode_against_oracle(gpu_lib, case, dtype):
     _check(gpu_lib, inp, f"{case} {dtype}")
 
 
-@pytest.mark.parametrize("dtype,tol", [("fp32", 1e-5), ("bf16", 1e-2)])
-def test_decode_agrees_with_the_forward_kernel(gpu_lib, dtype, tol):
-    """Same function as attn_sink_fwd: equal up to rounding order.  bf16 outputs may
-    differ by one unit in the last place of a bf16 value (2^-8 relative)."""
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_decode_agrees_with_the_forward_kernel(gpu_lib, dtype):
+    """Same function as attn_sink_fwd, and both normalise by the float32 sum of the
+    probabilities before they are rounded for the P.V product: equal up to rounding
+    order.  fp32: 1e-5 normwise.  bf16: LSE to 1e-6 normwise, and O within one bf16
+    unit in the last place of its largest element (at most 2^-7 normwise: the two
+    kernels round P under different running maxima, so an output element may land on
+    either side of a rounding boundary)."""
     for window in (0, 128):
         inp = decode_case([70, 4000, 9000], 4, 64, 8, 64, dtype, seed=21, window=window)
         a_o, a_lse = _decode(gpu_lib, inp)
         b_o, b_lse = _fwd(gpu_lib, inp)
-        compare(dict(o=_np(a_o), lse=_np(a_lse)), dict(o=_np(b_o), lse=_np(b_lse)), ("o", "lse"), tol,
-                f"decode vs fwd {dtype} w{window}")
+        a, b = dict(o=_np(a_o), lse=_np(a_lse)), dict(o=_np(b_o), lse=_np(b_lse))
+        if dtype == "fp32":
+            compare(a, b, ("o", "lse"), 1e-5, f"decode vs fwd {dtype} w{window}")
+            continue
+        compare(a, b, ("lse",), 1e-6, f"decode vs fwd lse {dtype} w{window}")
+        top = np.max(np.abs(b["o"]))
+        ulp_top = 2.0 ** (np.floor(np.log2(top)) - 7)  # bf16 spacing at the largest |O|
+        diff = np.max(np.abs(a["o"] - b["o"]))
+        print(f"[decode vs fwd] w{window}: max |diff| = {diff / ulp_top:.2f} bf16 ulp of max|O| "
+              f"({diff / top:.2e} normwise); {np.mean(a['o'] == b['o']):.3f} of elements equal", flush=True)
+        assert diff <= ulp_top, (diff, ulp_top)
 
 
 def test_decode_is_repeatable(gpu_lib):
