@@ -21,12 +21,13 @@ from typing import Optional
 
 import torch
 
-__all__ = ["load", "fwd", "fwd_decode", "fwd_decode_workspace_bytes", "merge", "bwd", "bwd_workspace_bytes",
+__all__ = ["load", "fwd", "fwd_decode", "fwd_decode_noalloc", "fwd_decode_workspace_bytes", "merge", "bwd", "bwd_workspace_bytes",
            "Shape", "AttnSinkError", "sink_attention", "timing_enable", "timing_read", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_sink.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+DECODE_SCRATCH_BYTES = 64 << 20  # ATTN_SINK_DECODE_SCRATCH_BYTES
 BF16, FP32 = 0, 1
 
 
@@ -73,6 +74,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_sink_fwd.restype = st
     lib.attn_sink_fwd_decode.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.attn_sink_fwd_decode.restype = st
+    lib.attn_sink_fwd_decode_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp]
+    lib.attn_sink_fwd_decode_noalloc.restype = st
     lib.attn_sink_fwd_decode_workspace_bytes.argtypes = [sp]
     lib.attn_sink_fwd_decode_workspace_bytes.restype = ctypes.c_size_t
     ci = ctypes.c_int
@@ -209,6 +212,30 @@ def fwd_decode(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None, ma
                                      _stream(q.device))
     if st != OK:
         raise AttnSinkError(st, "attn_sink_fwd_decode")
+    return o, lse
+
+
+def fwd_decode_noalloc(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None, max_seqlen_k=None,
+                       softmax_scale=None, causal=True, window=0, out=None, lse=None):
+    """fwd_decode() in the library's fixed per-GPU scratch (no workspace, no
+    allocation in the call itself; out= and lse= make the whole call allocation-free).
+    Calls that overlap on one GPU race on that scratch."""
+    _check_tensors(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k)
+    if max_seqlen_q is None:
+        max_seqlen_q = int((cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max().item()) if cu_seqlens_q.numel() > 1 else 0
+    if max_seqlen_k is None:
+        max_seqlen_k = int((cu_seqlens_k[1:] - cu_seqlens_k[:-1]).max().item()) if cu_seqlens_k.numel() > 1 else 0
+    if softmax_scale is None:
+        softmax_scale = q.shape[2] ** -0.5
+    shape = make_shape(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale, causal, window)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty(q.shape[1], q.shape[0], dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_buf("out", o, q.shape, q.dtype, q.device)
+    _check_buf("lse", lse, (q.shape[1], q.shape[0]), torch.float32, q.device)
+    st = _lib().attn_sink_fwd_decode_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(o),
+                                             _ptr(lse), _stream(q.device))
+    if st != OK:
+        raise AttnSinkError(st, "attn_sink_fwd_decode_noalloc")
     return o, lse
 
 

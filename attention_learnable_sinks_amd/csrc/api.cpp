@@ -142,6 +142,33 @@ DecodeWorkspace decode_layout(const attn_sink_shape* s) {
                                  s->max_seqlen_q, s->max_seqlen_k, s->window > 0 ? s->window : 0, s->head_dim);
 }
 
+// Checks shared by the two decoding entry points; fills `ws`.
+attn_sink_status decode_checks(const attn_sink_shape* shape, const void* q, const void* k, const void* v,
+                               const float* sinks, void* o, float* lse, DecodeWorkspace* ws) {
+  attn_sink_status st = check_shape(shape);
+  if (st != ATTN_SINK_OK) return st;
+  if (!decode_supported(shape->num_heads_q, shape->num_heads_kv, shape->max_seqlen_q)) return ATTN_SINK_ERR_UNSUPPORTED;
+  const bool any_q = shape->total_q > 0, any_k = shape->total_k > 0;
+  if (!sinks || (any_q && (!q || !o || !lse)) || (any_k && (!k || !v))) return ATTN_SINK_ERR_INVALID_ARG;
+  if (misaligned({q, k, v, o}, {sinks, lse})) return ATTN_SINK_ERR_INVALID_ARG;
+  *ws = decode_layout(shape);
+  return ATTN_SINK_OK;
+}
+
+DecodeArgs decode_args(const attn_sink_shape* shape, const void* q, const void* k, const void* v,
+                       const float* sinks, void* o, float* lse, const DecodeWorkspace& ws, void* workspace) {
+  DecodeArgs a;
+  a.f = fwd_args(shape, q, k, v, sinks, o, lse);
+  char* base = static_cast<char*>(workspace);
+  a.part_o = reinterpret_cast<float*>(base + ws.part_o);
+  a.part_ml = reinterpret_cast<float*>(base + ws.part_ml);
+  a.chunk = ws.chunk;
+  a.max_chunks = ws.max_chunks;
+  a.cols = ws.cols;
+  a.hw = ws.hw;
+  return a;
+}
+
 }  // namespace
 }  // namespace attn_sink
 
@@ -171,29 +198,43 @@ size_t attn_sink_fwd_decode_workspace_bytes(const attn_sink_shape* shape) {
 attn_sink_status attn_sink_fwd_decode(const attn_sink_shape* shape, const void* q, const void* k, const void* v,
                                       const float* sinks, void* o, float* lse, void* workspace,
                                       size_t workspace_bytes, hipStream_t stream) {
-  attn_sink_status st = check_shape(shape);
+  DecodeWorkspace ws;
+  attn_sink_status st = decode_checks(shape, q, k, v, sinks, o, lse, &ws);
   if (st != ATTN_SINK_OK) return st;
-  if (!decode_supported(shape->num_heads_q, shape->num_heads_kv, shape->max_seqlen_q)) return ATTN_SINK_ERR_UNSUPPORTED;
-  const bool any_q = shape->total_q > 0, any_k = shape->total_k > 0;
-  if (!sinks || (any_q && (!q || !o || !lse)) || (any_k && (!k || !v))) return ATTN_SINK_ERR_INVALID_ARG;
-  if (misaligned({q, k, v, o}, {sinks, lse})) return ATTN_SINK_ERR_INVALID_ARG;
-  const DecodeWorkspace ws = decode_layout(shape);
   if (!workspace || workspace_bytes < ws.total || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
     return ATTN_SINK_ERR_WORKSPACE;
-  if (!any_q) return ATTN_SINK_OK;
-  DecodeArgs a;
-  a.f = fwd_args(shape, q, k, v, sinks, o, lse);
-  char* base = static_cast<char*>(workspace);
-  a.part_o = reinterpret_cast<float*>(base + ws.part_o);
-  a.part_ml = reinterpret_cast<float*>(base + ws.part_ml);
-  a.chunk = ws.chunk;
-  a.max_chunks = ws.max_chunks;
-  a.cols = ws.cols;
-  a.hw = ws.hw;
+  if (shape->total_q == 0) return ATTN_SINK_OK;
+  const DecodeArgs a = decode_args(shape, q, k, v, sinks, o, lse, ws, workspace);
   const int fp32 = shape->dtype == ATTN_SINK_FP32;
   st = timed_launch(K_DEC_PARTIAL, stream, [&] { return launch_decode_partial(a, fp32, stream); });
   if (st != ATTN_SINK_OK || ws.max_chunks <= 1) return st;  // one chunk: finished in place
   return timed_launch(K_DEC_MERGE, stream, [&] { return launch_decode_merge(a, fp32, stream); });
+}
+
+attn_sink_status attn_sink_fwd_decode_noalloc(const attn_sink_shape* shape, const void* q, const void* k,
+                                              const void* v, const float* sinks, void* o, float* lse,
+                                              hipStream_t stream) {
+  DecodeWorkspace ws;
+  attn_sink_status st = decode_checks(shape, q, k, v, sinks, o, lse, &ws);
+  if (st != ATTN_SINK_OK) return st;
+  if (ws.total > kDecodeScratchBytes) return ATTN_SINK_ERR_WORKSPACE;  // beyond the fixed scratch
+  // The scratch used is the current device's copy, so the stream must belong to it.
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return ATTN_SINK_ERR_HIP;
+  if (stream != nullptr) {
+    int sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return ATTN_SINK_ERR_HIP;
+    if (sdev != dev) return ATTN_SINK_ERR_INVALID_ARG;
+  }
+  void* base = nullptr;
+  if (decode_scratch(&base) != hipSuccess) return ATTN_SINK_ERR_HIP;
+  if (shape->total_q == 0) return ATTN_SINK_OK;
+  const DecodeArgs a = decode_args(shape, q, k, v, sinks, o, lse, ws, base);
+  const int fp32 = shape->dtype == ATTN_SINK_FP32;
+  // Launched without the timing records (their events would be created here).
+  if (launch_decode_partial(a, fp32, stream) != hipSuccess) return ATTN_SINK_ERR_HIP;
+  if (ws.max_chunks <= 1) return ATTN_SINK_OK;  // one chunk: finished in place
+  return launch_decode_merge(a, fp32, stream) == hipSuccess ? ATTN_SINK_OK : ATTN_SINK_ERR_HIP;
 }
 
 size_t attn_sink_bwd_workspace_bytes(const attn_sink_shape* shape) {

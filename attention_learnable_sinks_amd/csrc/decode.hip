@@ -34,6 +34,8 @@
 //     (folded 16 chunks at a time with a running M, which is the same sum).
 //   The results equal the forward kernel's up to rounding order; the summation
 //   order is fixed, so they are bitwise repeatable.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -381,6 +383,37 @@ DecodeWorkspace decode_workspace_layout(int fp32, int hq, int hkv, int num_seqs,
   w.total = w.part_ml + ((parts * 2 * sizeof(float) + 255) & ~(size_t)255);
   if (w.total == 0) w.total = 256;  // nothing to keep, but a valid shape never reports 0
   return w;
+}
+
+// ---------------------------------------------------------------- fixed scratch
+// The workspace of the allocation-free decoding entry point: one copy of this array
+// per GPU (each device that loads the library holds its own, until the process
+// ends).  Host code never passes the array's name to a kernel (on the host it is a
+// stand-in, not a device address): decode_scratch() looks the device address up
+// once per device and keeps it.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // the current device's copy
+    if (e != hipSuccess) return e;
+    if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255) != 0) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode_partial(const DecodeArgs& a, int fp32, hipStream_t stream) {

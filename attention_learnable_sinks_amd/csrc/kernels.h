@@ -86,6 +86,11 @@ DecodeWorkspace decode_workspace_layout(int fp32, int hq, int hkv, int num_seqs,
 // The query heads of one kv head times the rows of one sequence fill at most 32 columns.
 bool decode_supported(int hq, int hkv, int max_q);
 
+// Size of the decoding forward's fixed scratch (one static device array per GPU) and
+// its address on the current device (looked up on the device's first call, then kept).
+constexpr size_t kDecodeScratchBytes = (size_t)64 << 20;
+hipError_t decode_scratch(void** ptr);
+
 // Each launcher enqueues one kernel on `stream` and returns hipGetLastError().
 hipError_t launch_fwd(const FwdArgs& a, int fp32, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int fp32, hipStream_t stream);

@@ -136,6 +136,30 @@ attn_sink_status attn_sink_fwd_decode(const attn_sink_shape* shape,
  * invalid or unsupported shape). */
 size_t attn_sink_fwd_decode_workspace_bytes(const attn_sink_shape* shape);
 
+/* Bytes of the fixed scratch attn_sink_fwd_decode_noalloc works in. */
+#define ATTN_SINK_DECODE_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* attn_sink_fwd_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments (minus the workspace), the
+ * same kernels and bitwise the same results.  The partials live in a fixed
+ * scratch array of ATTN_SINK_DECODE_SCRATCH_BYTES that the library holds on each
+ * GPU it runs on, from that device's first call until the process ends; the call
+ * itself allocates nothing (no hipMalloc, no events: it records no timing).
+ * The scratch used is the current device's: `stream` must belong to the current
+ * device (else ATTN_SINK_ERR_INVALID_ARG).  A shape whose workspace
+ * (attn_sink_fwd_decode_workspace_bytes) exceeds ATTN_SINK_DECODE_SCRATCH_BYTES
+ * returns ATTN_SINK_ERR_WORKSPACE before anything is enqueued.  Every call on one
+ * GPU shares that GPU's scratch and finds the previous call's contents there (no
+ * part of it needs clearing: every partial read is written first by the same
+ * call); calls that overlap in time on one GPU (different streams or threads) race
+ * on it and must be serialised by the caller. */
+attn_sink_status attn_sink_fwd_decode_noalloc(const attn_sink_shape* shape,
+                                              const void* q, const void* k, const void* v,
+                                              const float* sinks,
+                                              void* o, float* lse,
+                                              hipStream_t stream);
+
 /* Bytes of device workspace attn_sink_bwd needs for `shape` (0 on invalid shape). */
 size_t attn_sink_bwd_workspace_bytes(const attn_sink_shape* shape);
 

@@ -47,7 +47,8 @@ def test_head_dim_128_is_accepted(lib):
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["attn_sink_fwd", "attn_sink_bwd", "attn_sink_bwd_workspace_bytes",
-                                  "attn_sink_fwd_decode", "attn_sink_fwd_decode_workspace_bytes", "attn_sink_merge",
+                                  "attn_sink_fwd_decode", "attn_sink_fwd_decode_workspace_bytes",
+                                  "attn_sink_fwd_decode_noalloc", "attn_sink_merge",
                                   "attn_sink_status_string", "attn_sink_timing_enable", "attn_sink_timing_read"])
 
 
@@ -322,3 +323,16 @@ def test_merge_rejects_misaligned_tensor(lib, slot, by):
 def test_rejects_misaligned_cu_seqlens(lib, field):
     s = _shape(**{field: FAKE + 2})
     assert lib.attn_sink_fwd(ctypes.byref(s), *[FAKE] * 6, None) == als.ERR_INVALID_ARG
+
+
+def test_noalloc_decode_refuses_shapes_beyond_its_scratch(lib):
+    """The allocation-free decoding call rejects, before any device work, a shape
+    whose workspace exceeds the fixed scratch (64 sequences x 65,535-key caches)."""
+    lib.attn_sink_fwd_decode_noalloc.argtypes = [ctypes.POINTER(als.Shape)] + [ctypes.c_void_p] * 7
+    big = _decode_shape(num_seqs=64, total_q=64 * 4, max_seqlen_q=4, total_k=64 * 65535, max_seqlen_k=65535)
+    need = lib.attn_sink_fwd_decode_workspace_bytes(ctypes.byref(big))
+    assert need > als.DECODE_SCRATCH_BYTES
+    assert lib.attn_sink_fwd_decode_noalloc(ctypes.byref(big), *[FAKE] * 6, None) == als.ERR_WORKSPACE
+    for kw, status in BAD_SHAPES:  # the shape checks come first, as in attn_sink_fwd_decode
+        s = _decode_shape(**kw)
+        assert lib.attn_sink_fwd_decode_noalloc(ctypes.byref(s), *[FAKE] * 6, None) == status, kw
