@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn_sink.so")
-SOURCES = ["api.cpp", "fwd.hip", "bwd.hip", "decode.hip", "merge.hip"]
+SOURCES = ["api.cpp", "layout.cpp", "fwd.hip", "bwd.hip", "decode.hip", "merge.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU instructions.

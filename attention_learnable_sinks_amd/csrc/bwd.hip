@@ -41,7 +41,7 @@ namespace attn_sink {
 // ----------------------------------------------------------------------------- 1. dQ
 template <typename T, int D>
 struct DqCfg {
-  static constexpr int BM = 128;  // query rows per workgroup (4 wavefronts x 32)
+  static constexpr int BM = kDqRows;  // query rows per workgroup (4 wavefronts x 32)
   static constexpr int BN = 64;   // keys per tile
   static constexpr int THREADS = 256;
   static constexpr int TILE = tile_elems_d<T, D>(BN);
@@ -307,7 +307,7 @@ template <typename T, int D>
 struct DkvCfg {
   static constexpr int BMB = 64;       // queries per tile
   static constexpr int THREADS = 256;  // 4 wavefronts
-  static constexpr int BNB = 128;      // keys per key tile (32 per wavefront)
+  static constexpr int BNB = kDkvKeys;  // keys per key tile (32 per wavefront)
   static constexpr int TILE = tile_elems_d<T, D>(BMB);
   // workgroups resident per compute unit (bf16 at d = 64 fits two; the others one)
   static constexpr int PER_CU = (sizeof(T) == 2 && D == 64) ? 2 : 1;
@@ -636,80 +636,6 @@ __global__ __launch_bounds__(256) void bwd_finish_kernel(BwdArgs a) {
 }
 
 // ----------------------------------------------------------------------------- launchers
-static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-// Head-packed dQ tiles (as the forward's) on sliding-window layers: G = Hq / Hkv > 1
-// dividing the 128 rows of a tile, and the (sequence x tile) grid row within 65535.
-static bool dq_head_packed(int hq, int hkv, int num_seqs, int max_q, int window) {
-  constexpr int BM = DqCfg<bf16, 64>::BM;
-  const int G = hq / hkv;
-  if (window <= 0 || G < 2 || BM % G != 0) return false;
-  return ((long long)max_q * G + BM - 1) / BM * num_seqs <= 65535;
-}
-
-// Row tiles per sequence of the dQ grid (one dS_h partial per head and row tile).
-static int dq_tiles(int hq, int hkv, int num_seqs, int max_q, int window) {
-  constexpr int BM = DqCfg<bf16, 64>::BM;
-  const int per = dq_head_packed(hq, hkv, num_seqs, max_q, window) ? BM / (hq / hkv) : BM;
-  return (max_q + per - 1) / per;
-}
-
-int bwd_head_splits(int hq, int hkv, int total_k, int num_seqs, int causal, int window, int d, int fp32) {
-  // The dK/dV grid has one workgroup per (sequence, kv head, head split, folded pair
-  // of 128-key tiles); 256 or 512 run at once (one or two per compute unit, by the
-  // variant's registers).  Splitting the
-  // query heads of a kv head over s workgroups divides each workgroup's work by s
-  // but multiplies the grid by s and adds float32 partials (written here, read back
-  // by the finish kernel).  Estimated time, in microseconds:
-  //   rounds(s) x (group / s) x steps x 2.25  +  partial bytes(s) / 5 TB/s
-  // where steps is the number of (query head, 64-row tile) steps one folded pair
-  // takes for one head (from the mean sequence length, the mask and the window) and
-  // 2.25 us is the measured time of one such step.  Pick the cheapest s (the fewest
-  // splits on a tie).
-  const int group = hq / hkv;
-  const long long bnb = DkvCfg<bf16, 64>::BNB;  // keys per tile
-  long long pairs = (total_k + 2 * bnb - 1) / (2 * bnb) + num_seqs / 2;  // folded pairs (approx.)
-  if (pairs < 1) pairs = 1;
-  const long long n = num_seqs > 0 ? (long long)total_k / num_seqs : total_k;  // mean sequence length
-  long long steps;
-  if (window > 0) {
-    const long long w = window < n ? window : n;
-    steps = 2 * ((w + bnb + 63) / 64 + 1);  // each tile of the pair sees about window + bnb rows
-  } else {
-    steps = causal ? n / 64 + bnb / 64 : 2 * (n / 64 + 1);
-  }
-  if (steps < 1) steps = 1;
-  const long long kConcurrent = 256LL * ((!fp32 && d == 64) ? DkvCfg<bf16, 64>::PER_CU : DkvCfg<float, 64>::PER_CU);
-  const double part_bytes = 2.0 * 2.0 * (double)total_k * hkv * d * 4.0;  // dK + dV, written and read, per split
-  int best = 1;
-  double best_t = 0.0;
-  for (int sp = 1; sp <= group && group % sp == 0; sp *= 2) {
-    const long long rounds = (pairs * hkv * sp + kConcurrent - 1) / kConcurrent;
-    const double t = (double)rounds * (double)(group / sp) * (double)steps * 2.25 + (sp > 1 ? sp * part_bytes / 5e6 : 0.0);
-    if (sp == 1 || t < best_t) {
-      best = sp;
-      best_t = t;
-    }
-  }
-  return best;
-}
-
-BwdWorkspace bwd_workspace_layout(int hq, int hkv, int total_q, int total_k, int num_seqs, int max_q, int causal,
-                                  int window, int d, int fp32) {
-  BwdWorkspace w;
-  // one dS_h partial per (head, sequence, dQ row tile): the dQ workgroups write them
-  w.pre_blocks = num_seqs * dq_tiles(hq, hkv, num_seqs, max_q, window);
-  w.splits = bwd_head_splits(hq, hkv, total_k, num_seqs, causal, window, d, fp32);
-  size_t o = 0;
-  w.rowstat = o;     o = align256(o + (size_t)hq * 2 * total_q * 4);
-  w.dsink_part = o;  o = align256(o + (size_t)hq * w.pre_blocks * 4);
-  const size_t part = w.splits > 1 ? (size_t)w.splits * total_k * hkv * d * 4 : 0;
-  w.dk_part = o;     o = align256(o + part);
-  w.dv_part = o;     o = align256(o + part);
-  w.total = o;
-  return w;
-}
-
 template <typename T, int D>
 static void launch_bwd_dq_t(const BwdArgs& a, hipStream_t stream) {
   const FwdArgs& f = a.f;

@@ -41,10 +41,9 @@
 
 namespace attn_sink {
 
-constexpr int kDecBN = 32;    // keys per tile
-constexpr int kDecCols = 32;  // (query head, row) columns per kv head
-constexpr int kDecWaves = 4;  // wavefronts (kv heads) per workgroup at most
-constexpr int kDecChunk = 32; // key tiles per chunk (1024 keys)
+constexpr int kDecBN = kDecodeKeys;      // keys per tile
+constexpr int kDecCols = kDecodeCols;    // (query head, row) columns per kv head
+constexpr int kDecWaves = kDecodeWaves;  // wavefronts (kv heads) per workgroup at most
 
 // LDS stages per wavefront.  bf16: two, so the next tile's loads are in flight while
 // the wavefront computes on the current one; 4 wavefronts x 2 stages x 8 KB = 64 KB,
@@ -349,40 +348,6 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
       static_cast<T*>(f.o)[orow * D + d + 64 * j] = from_f32<T>(l > 0.f ? o[j] / l : 0.f);
     if (d == 0) f.lse[(size_t)head * f.total_q + sq.start + row] = l > 0.f ? (mm + fast_log2(l)) * kLn2 : -INFINITY;
   }
-}
-
-bool decode_supported(int hq, int hkv, int max_q) { return (long long)(hq / hkv) * max_q <= kDecCols; }
-
-DecodeWorkspace decode_workspace_layout(int fp32, int hq, int hkv, int num_seqs, int max_q, int max_k, int window,
-                                        int d) {
-  DecodeWorkspace w;
-  (void)fp32;
-  // kv heads per workgroup: the largest divisor of hkv up to kDecWaves.
-  w.hw = 1;
-  for (int d = 1; d <= kDecWaves; ++d)
-    if (hkv % d == 0) w.hw = d;
-  // Visible key tiles of one sequence at most (a window may straddle one more tile).
-  long long span = max_k;
-  if (window > 0 && (long long)window + max_q - 1 < span) span = (long long)window + max_q - 1;
-  const long long tiles = max_q > 0 ? (span + kDecBN - 1) / kDecBN + (window > 0 ? 1 : 0) : 0;
-  // A fixed chunk, so a sequence's result depends on that sequence alone and not on
-  // the rest of the batch (batch invariance: the same rounding order whatever the
-  // batch size or the longest cache).  1024 keys: a partial costs under 1% of the
-  // bytes its chunk reads, a 128-key window (at most 5 tiles) needs no merge, and a
-  // 64-sequence rollout step of 1k-16k caches gives about a thousand workgroups.
-  // The grid limit (65535 chunks) is far beyond max_seqlen_k <= 65535 * 128.
-  const long long chunk = kDecChunk;
-  (void)num_seqs;
-  w.chunk = (int)chunk;
-  w.max_chunks = (int)(tiles > 0 ? (tiles + chunk - 1) / chunk : 1);
-  w.cols = (hq / hkv) * max_q;
-  if (w.cols < 1) w.cols = 1;
-  const size_t parts = w.max_chunks > 1 ? (size_t)num_seqs * hkv * w.max_chunks * w.cols : 0;
-  w.part_o = 0;
-  w.part_ml = (parts * d * sizeof(float) + 255) & ~(size_t)255;
-  w.total = w.part_ml + ((parts * 2 * sizeof(float) + 255) & ~(size_t)255);
-  if (w.total == 0) w.total = 256;  // nothing to keep, but a valid shape never reports 0
-  return w;
 }
 
 // ---------------------------------------------------------------- fixed scratch

@@ -68,6 +68,18 @@ enum KernelId {
 };
 const char* kernel_name(int id);
 
+// Tile shapes the host-side layout shares with the kernels (static_assert'ed there).
+constexpr int kDqRows = 128;      // query rows per dQ workgroup
+constexpr int kDkvKeys = 128;     // keys per dK/dV workgroup tile
+constexpr int kDecodeKeys = 32;   // keys per decoding tile
+constexpr int kDecodeCols = 32;   // (query head, row) columns per kv head in the decoding kernels
+constexpr int kDecodeWaves = 4;   // kv heads (wavefronts) per decoding workgroup at most
+constexpr int kDecodeChunk = 32;  // key tiles per decoding chunk (1024 keys)
+
+// Head-packed dQ tiles (window layers) and dQ row tiles per sequence.
+bool dq_head_packed(int hq, int hkv, int num_seqs, int max_q, int window);
+int dq_tiles(int hq, int hkv, int num_seqs, int max_q, int window);
+
 // Workspace layout for a backward call; offsets in bytes from the workspace base.
 struct BwdWorkspace {
   size_t rowstat, dsink_part, dk_part, dv_part, total;
