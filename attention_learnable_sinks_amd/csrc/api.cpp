@@ -101,11 +101,12 @@ attn_sink_status check_shape(const attn_sink_shape* s) {
   // grid limits: y is the tile index (<= 65535); x is heads * sequences
   if ((long long)s->num_heads_q * s->num_seqs > 0x7fffffffLL) return ATTN_SINK_ERR_UNSUPPORTED;
   if (s->max_seqlen_q > 65535LL * 128 || s->max_seqlen_k > 65535LL * 128) return ATTN_SINK_ERR_UNSUPPORTED;
-  // Each kernel reads one head of one sequence through a buffer descriptor whose
-  // byte range (rows x row pitch) must fit in 32 bits.
+  // Each kernel reads one head of one sequence through a buffer descriptor with
+  // 32-bit byte offsets; a tile (at most 128 rows) may start on the last row, so
+  // (rows + 128) x row pitch must fit in 32 bits.
   const long long esize = s->dtype == ATTN_SINK_FP32 ? 4 : 2;
-  if ((long long)s->max_seqlen_q * s->num_heads_q * s->head_dim * esize >= (1LL << 32) ||
-      (long long)s->max_seqlen_k * s->num_heads_kv * s->head_dim * esize >= (1LL << 32))
+  if ((s->max_seqlen_q + 128LL) * s->num_heads_q * s->head_dim * esize >= (1LL << 32) ||
+      (s->max_seqlen_k + 128LL) * s->num_heads_kv * s->head_dim * esize >= (1LL << 32))
     return ATTN_SINK_ERR_UNSUPPORTED;
   // 32-bit row indices inside the kernels
   if ((long long)s->total_q * s->num_heads_q * s->head_dim > 0x7fffffffLL * 4LL) return ATTN_SINK_ERR_UNSUPPORTED;

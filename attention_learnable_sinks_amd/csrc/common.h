@@ -292,11 +292,18 @@ __device__ inline float frag_dot(typename Mfma<T>::Frag a, typename Mfma<T>::Fra
 
 // ---------------------------------------------------------------- global <-> LDS staging
 // A tile of `ROWS` rows x 64 columns of one head, moved as 16-byte chunks (CPR per
-// row) with raw buffer loads: the buffer descriptor covers exactly the sequence's
-// rows of this head, so the per-thread offset is a constant VGPR, the tile offset
-// is a scalar, and chunks past the last row read as zero (buffer range checking)
-// without any branch or address arithmetic in the loop.
+// row) with raw buffer loads through one descriptor that covers exactly the
+// sequence's rows of this head.  The whole byte offset of a chunk (the tile's first
+// row plus the lane's row and column) goes in the VGPR offset: the raw-buffer range
+// check compares that offset (not the scalar one) with the descriptor's size, so
+// chunks past the last row read as zero and nothing beyond the sequence is touched.
+// Offsets are 32-bit: the caller guarantees (nrows + 128) * row_bytes < 2^32, and
+// tiles start at a row below nrows.
 constexpr int kBufferWord3 = 0x00020000;  // gfx9-family raw buffer descriptor, dword 3
+
+__device__ inline __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
 
 template <typename T, int ROWS, int THREADS>
 struct Stager {
@@ -309,10 +316,10 @@ struct Stager {
   uint32_t voff[N];
   uint4 reg[N];
   // base: element (row 0, column 0) of the head; rows are row_stride elements apart;
-  // nrows rows are readable (the caller guarantees nrows * row_stride * sizeof(T) < 2^32).
+  // nrows rows are readable.
   __device__ inline void init(const T* base, size_t row_stride, int nrows, int tid) {
     row_bytes = (uint32_t)(row_stride * sizeof(T));
-    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), (short)0, (int)(nrows * row_bytes), kBufferWord3);
+    rsrc = rows_rsrc(base, (uint32_t)nrows * row_bytes);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int ch = tid + THREADS * i;
@@ -321,10 +328,10 @@ struct Stager {
   }
   // Load the tile whose first row is row0 (rows >= nrows read as zero).
   __device__ inline void load(int row0) {
-    const uint32_t soff = (uint32_t)row0 * row_bytes;
+    const uint32_t toff = (uint32_t)row0 * row_bytes;
 #pragma unroll
     for (int i = 0; i < N; ++i)
-      reg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[i], soff, 0));
+      reg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[i] + toff, 0, 0));
   }
   __device__ inline void store(T* tile, int tid) const {
 #pragma unroll
@@ -353,11 +360,12 @@ struct Stager {
 __device__ inline uint32_t lds_address(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
-__device__ inline void lds_dma_b128(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds) : "memory");
+// The scalar offset is 0: the whole offset is in voff, where the range check sees it.
+__device__ inline void lds_dma_b128(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
 }
-__device__ inline void lds_dma_b32(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("buffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds) : "memory");
+__device__ inline void lds_dma_b32(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
 }
 
 // Wait for every outstanding vector-memory load.  Called once after a kernel's
@@ -397,7 +405,7 @@ struct TileLoader<bf16, ROWS, THREADS> {
   int first_slot;  // first LDS slot (of 64) written by this wavefront's instructions
   __device__ inline void init(const bf16* base, size_t row_stride, int nrows, int tid) {
     row_bytes = (uint32_t)(row_stride * sizeof(bf16));
-    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), (short)0, (int)(nrows * row_bytes), kBufferWord3);
+    rsrc = rows_rsrc(base, (uint32_t)nrows * row_bytes);
     const int lane = tid & 63;
     first_slot = __builtin_amdgcn_readfirstlane(tid >> 6) * N * 64;
 #pragma unroll
@@ -409,10 +417,10 @@ struct TileLoader<bf16, ROWS, THREADS> {
     }
   }
   __device__ inline void issue(int row0, bf16* tile) {
-    const uint32_t soff = (uint32_t)row0 * row_bytes;
 #if defined(__HIP_DEVICE_COMPILE__)  // device-only asm
+    const uint32_t toff = (uint32_t)row0 * row_bytes;
 #pragma unroll
-    for (int n = 0; n < N; ++n) lds_dma_b128(rsrc, voff[n], soff, lds_address(tile + (first_slot + n * 64) * 8));
+    for (int n = 0; n < N; ++n) lds_dma_b128(rsrc, voff[n] + toff, lds_address(tile + (first_slot + n * 64) * 8));
 #endif
   }
   __device__ inline void finish() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
@@ -461,13 +469,11 @@ struct TileLoaderD {
 // wavefront instruction (lane i -> float i); rows past `nrows` read as zero.
 struct RowLoader {
   __amdgpu_buffer_rsrc_t rsrc;
-  __device__ inline void init(const float* base, int nrows) {
-    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, nrows * 4, kBufferWord3);
-  }
+  __device__ inline void init(const float* base, int nrows) { rsrc = rows_rsrc(base, (uint32_t)nrows * 4u); }
   // Call from one whole wavefront; finish with the tile loads' wait (vmcnt(0)).
   __device__ inline void issue(int row0, float* lds, int lane) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    lds_dma_b32(rsrc, (uint32_t)lane * 4u, (uint32_t)row0 * 4u, lds_address(lds));
+    lds_dma_b32(rsrc, (uint32_t)(row0 + lane) * 4u, lds_address(lds));
 #endif
   }
 };

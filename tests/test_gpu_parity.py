@@ -373,3 +373,30 @@ def test_backward_on_the_oracle_forward_4k_group0(gpu_lib):
     compare(gpu, ref, ("dq", "dk", "dv", "dsinks"), TOL["bf16"], "bwd on oracle fwd gptoss_4k group 0")
     compare_dsinks_per_head(gpu, ref, range(8), TOL["bf16"], "bwd on oracle fwd gptoss_4k group 0",
                             terms=sink_terms(inp, ref))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("window", [0, 50])
+def test_rows_past_a_sequence_are_never_read(gpu_lib, dtype, window):
+    """Tiles that straddle a sequence's end must see zeros, not the rows that follow it
+    in memory: with the next sequence's Q, K, V and dO set to NaN, the first
+    sequence's O, LSE and dQ equal those of a call on it alone, bitwise, and its dK and
+    dV agree to the rounding of the head-split partials (the split count depends on
+    the batch); a masked product 0 x NaN would otherwise poison them."""
+    n0, n1 = 100, 77  # the first sequence ends inside a 64- and a 128-row tile
+    inp = random_case([n0, n1], 8, 2, 64, dtype, seed=41 + window, window=window)
+    for key in ("q", "k", "v", "dout"):
+        inp[key][n0:] = float("nan")
+    print(f"[case] rows past a sequence {dtype} w{window}", flush=True)
+    both = gpu_fwd_bwd(gpu_lib, inp)
+    one = dict(inp, q=inp["q"][:n0], k=inp["k"][:n0], v=inp["v"][:n0], dout=inp["dout"][:n0],
+               cu_seqlens=torch.tensor([0, n0], dtype=torch.int32), max_seqlen=n0)
+    alone = gpu_fwd_bwd(gpu_lib, one)
+    assert np.all(np.isfinite(alone["o"])) and np.all(np.isfinite(alone["dk"]))
+    assert np.array_equal(both["o"][:n0], alone["o"])
+    assert np.array_equal(both["lse"][:, :n0], alone["lse"])
+    assert np.array_equal(both["dq"][:n0], alone["dq"])
+    for key in ("dk", "dv"):
+        assert np.all(np.isfinite(both[key][:n0])), key
+        err = np.max(np.abs(both[key][:n0] - alone[key])) / np.max(np.abs(alone[key]))
+        assert err <= TOL[dtype], (key, err)
