@@ -93,8 +93,12 @@ __global__ __launch_bounds__(256, (DqCfg<T, D>::MIN_WG)) void bwd_dq_kernel(BwdA
   const int qw = PKH ? qs + (32 * w) / G : qs + 32 * w;                    // first position of the wavefront
   const int qw_last = PKH ? qs + (32 * w + 31) / G : qw + 31;              // its last position
   const int qw_end = min(qw_last + 1, nq);
+  // The wavefront's rows see keys in [wlo, whi); all of them see [wlo_all, whi_all)
+  // (both ends of a row's key interval are nondecreasing in the row).
   int whi = f.causal ? clampi(qw_end - 1 + off + 1, 0, nk) : nk;
   int wlo = f.window > 0 ? clampi(qw + off - f.window + 1, 0, nk) : 0;
+  const int whi_all = f.causal ? clampi(qw + off + 1, 0, nk) : nk;
+  const int wlo_all = f.window > 0 ? clampi(qw_end - 1 + off - f.window + 1, 0, nk) : 0;
   if (qw >= nq) whi = wlo = 0;
 
   const size_t kv_row = (size_t)f.hkv * D, q_row = (size_t)f.hq * D;
@@ -136,8 +140,8 @@ __global__ __launch_bounds__(256, (DqCfg<T, D>::MIN_WG)) void bwd_dq_kernel(BwdA
   kld.init(kbase_p, kv_row, nk, tid);
   vld.init(vbase_p, kv_row, nk, tid);
   if (kt_begin < kt_end) {
-    kld.issue(kt_begin * C::BN, smem);
-    vld.issue(kt_begin * C::BN, smem + C::TILE);
+    kld.issue_rebased(kt_begin * C::BN, smem);
+    vld.issue_rebased(kt_begin * C::BN, smem + C::TILE);
     kld.finish();
     vld.finish();
   }
@@ -162,9 +166,19 @@ __global__ __launch_bounds__(256, (DqCfg<T, D>::MIN_WG)) void bwd_dq_kernel(BwdA
   vmem_drain();
   __syncthreads();
 
-  // One tile: S^T, dP^T, P^T, dS^T, dQ^T += K^T dS^T; FULL tiles need no mask.
+  // One tile: S^T, dP^T, P^T, dS^T, dQ^T += K^T dS^T.  FULL tiles need no mask; in
+  // the others only the 32-key halves that not every row of the wavefront sees in
+  // full take the per-element mask.
   auto body = [&](const T* Ks, const T* Vs, int kbase, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
+    int masked = 0;  // bit mt: keys kbase + 32 mt ..+32
+    if constexpr (!FULL) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int k = kbase + 32 * mt;
+        masked |= (k >= wlo_all && k + 32 <= whi_all) ? 0 : 1 << mt;
+      }
+    }
     f32x16 st[2], dpt[2];  // S^T, dP^T: [64 keys x 32 q]
     // Issue priority while this wavefront feeds the matrix cores, so the other
     // wavefronts on the SIMD fill the vector ALUs meanwhile (measured faster here).
@@ -191,15 +205,20 @@ __global__ __launch_bounds__(256, (DqCfg<T, D>::MIN_WG)) void bwd_dq_kernel(BwdA
     __builtin_amdgcn_s_setprio(0);
     float tsum[2];  // the tile's row sums of dS^T, one chain per 32 keys
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[mt][r] = fast_exp2(fmaf(st[mt][r], sl2, -lse2));  // P^T
+      if (!FULL && (masked >> mt & 1)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)  // key kbase + 4h + (32 mt + 8 (r/4) + r%4)
+          st[mt][r] = in_span(kbase + 4 * h + 32 * mt + 8 * (r / 4) + r % 4, row_keys) ? st[mt][r] : 0.f;
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pv = fast_exp2(fmaf(st[mt][r], sl2, -lse2));  // P^T
-        if constexpr (!FULL)  // key kbase + 4h + (32 mt + 8 (r/4) + r%4)
-          pv = in_span(kbase + 4 * h + 32 * mt + 8 * (r / 4) + r % 4, row_keys) ? pv : 0.f;
-        st[mt][r] = pv * (sizeof(T) == 2 ? dpt[mt][r] : dpt[mt][r] - dd);  // dS^T = P^T (dP^T - D)
+        st[mt][r] *= sizeof(T) == 2 ? dpt[mt][r] : dpt[mt][r] - dd;  // dS^T = P^T (dP^T - D)
         tsum[mt] = r == 0 ? st[mt][r] : tsum[mt] + st[mt][r];
       }
+    }
     dsum += tsum[0] + tsum[1];
     // dQ^T[d x q] += K^T[d x keys] . dS^T[keys x q]
     __builtin_amdgcn_s_setprio(1);
@@ -217,8 +236,8 @@ __global__ __launch_bounds__(256, (DqCfg<T, D>::MIN_WG)) void bwd_dq_kernel(BwdA
     const bool more = kt + 1 < kt_end;
     T* nb = smem + (buf ^ 1) * 2 * C::TILE;  // read in the previous step, before its barrier
     if (more) {
-      kld.issue((kt + 1) * C::BN, nb);
-      vld.issue((kt + 1) * C::BN, nb + C::TILE);
+      kld.issue_rebased((kt + 1) * C::BN, nb);
+      vld.issue_rebased((kt + 1) * C::BN, nb + C::TILE);
     }
     const int kbase = kt * C::BN;
     const T* Ks = smem + buf * 2 * C::TILE;

@@ -298,7 +298,9 @@ __device__ inline float frag_dot(typename Mfma<T>::Frag a, typename Mfma<T>::Fra
 // check compares that offset (not the scalar one) with the descriptor's size, so
 // chunks past the last row read as zero and nothing beyond the sequence is touched.
 // Offsets are 32-bit: the caller guarantees (nrows + 128) * row_bytes < 2^32, and
-// tiles start at a row below nrows.
+// tiles start at a row below nrows.  Where registers are tight, issue_rebased()
+// moves the tile's first row into the descriptor instead (base + row0 rows, sized
+// to the rows left), which costs scalar instructions and no vector register.
 constexpr int kBufferWord3 = 0x00020000;  // gfx9-family raw buffer descriptor, dword 3
 
 __device__ inline __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, uint32_t bytes) {
@@ -400,10 +402,14 @@ struct TileLoader<bf16, ROWS, THREADS> {
   static constexpr int N = ROWS * 8 / THREADS;  // 16-byte slots per thread
   static_assert(ROWS * 8 % THREADS == 0, "tile must split evenly over the threads");
   __amdgpu_buffer_rsrc_t rsrc;
+  const bf16* base_;
+  int nrows_;
   uint32_t row_bytes;
   uint32_t voff[N];
   int first_slot;  // first LDS slot (of 64) written by this wavefront's instructions
   __device__ inline void init(const bf16* base, size_t row_stride, int nrows, int tid) {
+    base_ = base;
+    nrows_ = nrows;
     row_bytes = (uint32_t)(row_stride * sizeof(bf16));
     rsrc = rows_rsrc(base, (uint32_t)nrows * row_bytes);
     const int lane = tid & 63;
@@ -423,6 +429,14 @@ struct TileLoader<bf16, ROWS, THREADS> {
     for (int n = 0; n < N; ++n) lds_dma_b128(rsrc, voff[n] + toff, lds_address(tile + (first_slot + n * 64) * 8));
 #endif
   }
+  __device__ inline void issue_rebased(int row0, bf16* tile) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const char* p = reinterpret_cast<const char*>(base_) + (size_t)row0 * row_bytes;
+    const __amdgpu_buffer_rsrc_t r = rows_rsrc(p, (uint32_t)max(nrows_ - row0, 0) * row_bytes);
+#pragma unroll
+    for (int n = 0; n < N; ++n) lds_dma_b128(r, voff[n], lds_address(tile + (first_slot + n * 64) * 8));
+#endif
+  }
   __device__ inline void finish() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 };
 
@@ -440,6 +454,7 @@ struct TileLoader<float, ROWS, THREADS> {
     st.load(row0);
     dst = tile;
   }
+  __device__ inline void issue_rebased(int row0, float* tile) { issue(row0, tile); }
   __device__ inline void finish() { st.store(dst, tid_); }
 };
 
@@ -458,6 +473,10 @@ struct TileLoaderD {
   __device__ inline void issue(int row0, T* tile) {
 #pragma unroll
     for (int i = 0; i < BLOCKS; ++i) sub[i].issue(row0, tile + i * tile_elems<T>(ROWS));
+  }
+  __device__ inline void issue_rebased(int row0, T* tile) {
+#pragma unroll
+    for (int i = 0; i < BLOCKS; ++i) sub[i].issue_rebased(row0, tile + i * tile_elems<T>(ROWS));
   }
   __device__ inline void finish() {
 #pragma unroll

@@ -107,8 +107,13 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::MIN_WG)) void fwd_kernel(FwdArg
   const int qw = PKH ? qs + (32 * w) / G : qs + 32 * w;                    // first position of the wavefront
   const int qw_end = min(PKH ? qs + (32 * w + 31) / G + 1 : qw + 32, nq);  // one past its last
   const bool wave_rows = qw < nq;
+  // Every row's keys form one interval [lo_i, hi_i) whose ends do not decrease with
+  // the row: the wavefront's rows see keys in [wlo, whi) and all of them see
+  // [wlo_all, whi_all).
   int whi = p.causal ? clampi(qw_end - 1 + off + 1, 0, nk) : nk;
   int wlo = p.window > 0 ? clampi(qw + off - p.window + 1, 0, nk) : 0;
+  const int whi_all = p.causal ? clampi(qw + off + 1, 0, nk) : nk;
+  const int wlo_all = p.window > 0 ? clampi(qw_end - 1 + off - p.window + 1, 0, nk) : 0;
   if (!wave_rows) whi = wlo = 0;
 
   const size_t kv_row = (size_t)p.hkv * D;
@@ -146,17 +151,39 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::MIN_WG)) void fwd_kernel(FwdArg
   kld.init(kbase_p, kv_row, nk, tid);
   vld.init(vbase_p, kv_row, nk, tid);
   if (kt_begin < kt_end) {
-    kld.issue(kt_begin * C::BN, smem);
-    vld.issue(kt_begin * C::BN, smem + C::TILE);
+    kld.issue_rebased(kt_begin * C::BN, smem);
+    vld.issue_rebased(kt_begin * C::BN, smem + C::TILE);
     kld.finish();
     vld.finish();
   }
   vmem_drain();
   __syncthreads();
 
-  // S^T of one tile [64 keys x 32 queries], masked to -inf outside the band when
-  // the tile straddles a band edge.
-  auto scores = [&](f32x16* st, const T* Ks, int kbase, auto full_tag) __attribute__((always_inline)) {
+  // Which 32-key halves of the tile at kbase any row of the wavefront sees (bit mt
+  // for keys kbase + 32 mt ..+32), and which of those every row sees in full; the
+  // others need the per-element mask.  Wavefront-uniform.
+  auto half_live = [&](int kbase) __attribute__((always_inline)) -> int {
+    int live = 0;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int a = kbase + 32 * mt;
+      live |= (a < whi && a + 32 > wlo) ? 1 << mt : 0;
+    }
+    return live;
+  };
+  auto half_full = [&](int kbase) __attribute__((always_inline)) -> int {
+    int full = 0;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int a = kbase + 32 * mt;
+      full |= (a >= wlo_all && a + 32 <= whi_all) ? 1 << mt : 0;
+    }
+    return full;
+  };
+  // S^T of one tile [64 keys x 32 queries].  Tiles that straddle a band edge are
+  // masked to -inf outside the band, per 32-key half: halves every row sees take no
+  // mask, halves no row sees none either (their probabilities are set to zero).
+  auto scores = [&](f32x16* st, const T* Ks, int kbase, int live, auto full_tag) __attribute__((always_inline)) {
     constexpr bool FULL = decltype(full_tag)::value;
     if constexpr (C::PACKED) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -168,13 +195,16 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::MIN_WG)) void fwd_kernel(FwdArg
     }
     if constexpr (C::PACKED) __builtin_amdgcn_s_setprio(0);
     if constexpr (!FULL) {
+      const int full = half_full(kbase);
       // key of register r in tile mt: kbase + 4h + (32 mt + 8 (r/4) + r%4), a constant per element
       const int k0 = kbase + 4 * h;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
+        if ((live & ~full) >> mt & 1) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          st[mt][r] = in_span(k0 + 32 * mt + 8 * (r / 4) + r % 4, row_keys) ? st[mt][r] : -INFINITY;
+          for (int r = 0; r < 16; ++r)
+            st[mt][r] = in_span(k0 + 32 * mt + 8 * (r / 4) + r % 4, row_keys) ? st[mt][r] : -INFINITY;
+        }
     }
   };
   // P = exp2(s * sl2 + neg_m) in place, rounded into operands; returns the lane's
@@ -182,11 +212,18 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::MIN_WG)) void fwd_kernel(FwdArg
   // the bf16 dot-product instruction that could sum the rounded operands directly
   // does not overlap with the MFMAs of the other wavefronts on the SIMD, while
   // adds do (measured: about 0.15 against 0.55 overlap); about 1% faster here.
-  auto probs = [&](f32x16* st, Frag* pf, float neg_m) __attribute__((always_inline)) -> float {
+  auto probs = [&](f32x16* st, Frag* pf, float neg_m, int live, auto full_tag) __attribute__((always_inline)) -> float {
+    constexpr bool FULL = decltype(full_tag)::value;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt) {
+      if (FULL || (live >> mt & 1)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[mt][r] = fast_exp2(fmaf(st[mt][r], sl2, neg_m));
+        for (int r = 0; r < 16; ++r) st[mt][r] = fast_exp2(fmaf(st[mt][r], sl2, neg_m));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[mt][r] = 0.f;
+      }
+    }
     float sum = 0.f;
 #pragma unroll
     for (int s = 0; s < NP; ++s) {
@@ -205,10 +242,12 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::MIN_WG)) void fwd_kernel(FwdArg
 
   // One tile: S^T, (mask), P^T, O^T += V^T P^T.
   auto body = [&](const T* Ks, const T* Vs, int kbase, auto full_tag) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    const int live = FULL ? 3 : half_live(kbase);
     f32x16 st[2];
     Frag pf[NP];
-    scores(st, Ks, kbase, full_tag);
-    float tsum = probs(st, pf, -m_run);  // m_run = -inf gives inf / NaN: caught below
+    scores(st, Ks, kbase, live, full_tag);
+    float tsum = probs(st, pf, -m_run, live, full_tag);  // m_run = -inf gives inf / NaN: caught below
     const bool over = !(tsum <= kTileSumMax);
     if (__any(over)) {
       // Slow path (rare): raise the running max to this tile's row max.  The K
@@ -217,12 +256,14 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::MIN_WG)) void fwd_kernel(FwdArg
       // depends on the other rows of the wavefront (a row computed alone, e.g. one
       // decode step, comes out bitwise the same as in a full forward).
       const bool row_over = halves_max(over ? 1.f : 0.f) > 0.f;  // either half of the row
-      scores(st, Ks, kbase, full_tag);
+      scores(st, Ks, kbase, live, full_tag);
       float mx = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
+        if (FULL || (live >> mt & 1)) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[mt][r]);
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[mt][r]);
+        }
       mx = halves_max(mx) * sl2;
       const float m_new = row_over ? fmaxf(m_run, mx) : m_run;
       const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);  // 0 when m_run = -inf
@@ -233,7 +274,7 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::MIN_WG)) void fwd_kernel(FwdArg
         for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
       m_run = m_new;
       // m_new = -inf: every score of the row is masked so far, exp2(-inf + 0) = 0.
-      tsum = probs(st, pf, m_new == -INFINITY ? 0.f : -m_new);
+      tsum = probs(st, pf, m_new == -INFINITY ? 0.f : -m_new, live, full_tag);
     }
     l_run += tsum;
     // O^T[d x q] += V^T[d x keys] . P^T[keys x q]
@@ -250,14 +291,14 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::MIN_WG)) void fwd_kernel(FwdArg
     constexpr bool FULL = decltype(full_tag)::value;
     const bool more = kt + 1 < kt_end;
     if (more) {  // nxt was last read in the previous step, before its barrier
-      kld.issue((kt + 1) * C::BN, nxt);
-      vld.issue((kt + 1) * C::BN, nxt + C::TILE);
+      kld.issue_rebased((kt + 1) * C::BN, nxt);
+      vld.issue_rebased((kt + 1) * C::BN, nxt + C::TILE);
     }
     const int kbase = kt * C::BN;
     if constexpr (FULL) {
       body(cur, cur + C::TILE, kbase, full_tag);
     } else {
-      if (kbase < whi && kbase + C::BN > wlo) body(cur, cur + C::TILE, kbase, full_tag);
+      if (kbase < whi && kbase + C::BN > wlo) body(cur, cur + C::TILE, kbase, full_tag);  // some half is live
     }
     if (more) {
       kld.finish();
