@@ -60,18 +60,20 @@ __global__ __launch_bounds__(256, (DqCfg<T, D>::MIN_WG)) void bwd_dq_kernel(BwdA
   __shared__ float red[PKH ? C::BM : 4];
 
   // PKH (head-packed tiles, sliding-window layers): the 128 rows of a tile are
-  // BM / G positions x the G query heads of one kv head (row r: position r / G,
-  // head r % G), as in the forward; blockIdx.y = sequence x its tiles.
+  // BM / G positions x the G query heads of one kv head (row r: position r >> lg,
+  // head r & (G - 1), G = 2^lg since it divides BM), as in the forward; the grid is
+  // (kv head, tile, sequence).
   const int G = f.hq / f.hkv;
-  const XcdSlot slot = xcd_slot(blockIdx.x, f.hkv, PKH ? 1 : G);
-  const int bmq = PKH ? C::BM / G : C::BM;  // query positions per workgroup
-  const int ntiles = PKH ? (f.max_q + bmq - 1) / bmq : (int)gridDim.y;  // row tiles per sequence
-  const int b = PKH ? (int)blockIdx.y / ntiles : slot.seq, g = slot.kv;
-  const int tile = PKH ? (int)blockIdx.y % ntiles : gridDim.y - 1 - blockIdx.y;
+  const int lg = PKH ? __builtin_ctz(G) : 0;
+  const XcdSlot slot = PKH ? XcdSlot{(int)blockIdx.z, (int)blockIdx.x, 0} : xcd_slot(blockIdx.x, f.hkv, G);
+  const int bmq = PKH ? C::BM >> lg : C::BM;  // query positions per workgroup
+  const int ntiles = (int)gridDim.y;           // row tiles per sequence
+  const int b = slot.seq, g = slot.kv;
+  const int tile = PKH ? (int)blockIdx.y : gridDim.y - 1 - blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index (uniform)
   const int h = lane >> 5, c = lane & 31;
-  const int head = PKH ? g * G + (32 * w + c) % G : g * G + slot.item;  // this lane's row's head
+  const int head = PKH ? g * G + ((32 * w + c) & (G - 1)) : g * G + slot.item;  // this lane's row's head
   const SeqBounds sq = seq_bounds(f.cu_q, b, f.total_q);
   const SeqBounds sk = seq_bounds(f.cu_k, b, f.total_k);
   const int nq = sq.len, nk = sk.len, off = nk - nq;
@@ -90,8 +92,8 @@ __global__ __launch_bounds__(256, (DqCfg<T, D>::MIN_WG)) void bwd_dq_kernel(BwdA
   fa.init(lane);
   const int khi = f.causal ? clampi(qe - 1 + off + 1, 0, nk) : nk;
   const int klo = f.window > 0 ? clampi(qs + off - f.window + 1, 0, nk) : 0;
-  const int qw = PKH ? qs + (32 * w) / G : qs + 32 * w;                    // first position of the wavefront
-  const int qw_last = PKH ? qs + (32 * w + 31) / G : qw + 31;              // its last position
+  const int qw = PKH ? qs + ((32 * w) >> lg) : qs + 32 * w;        // first position of the wavefront
+  const int qw_last = PKH ? qs + ((32 * w + 31) >> lg) : qw + 31;  // its last position
   const int qw_end = min(qw_last + 1, nq);
   // The wavefront's rows see keys in [wlo, whi); all of them see [wlo_all, whi_all)
   // (both ends of a row's key interval are nondecreasing in the row).
@@ -106,7 +108,7 @@ __global__ __launch_bounds__(256, (DqCfg<T, D>::MIN_WG)) void bwd_dq_kernel(BwdA
   const T* vbase_p = static_cast<const T*>(f.v) + (size_t)sk.start * kv_row + g * D;
 
   // Q and dO fragments (B operands of S^T = K Q^T and dP^T = V dO^T); lse and D of the lane's row.
-  const int qi = PKH ? qs + (32 * w + c) / G : qw + c;  // this lane's row's position
+  const int qi = PKH ? qs + ((32 * w + c) >> lg) : qw + c;  // this lane's row's position
   const bool qok = qi < nq;
   Span row_keys = keys_of_row(qi, off, nk, f.causal, f.window);  // the keys row qi sees
   if (!qok) row_keys.len = 0u;
@@ -660,7 +662,7 @@ static void launch_bwd_dq_t(const BwdArgs& a, hipStream_t stream) {
   const FwdArgs& f = a.f;
   const int tiles = dq_tiles(f.hq, f.hkv, f.num_seqs, f.max_q, f.window);
   if (dq_head_packed(f.hq, f.hkv, f.num_seqs, f.max_q, f.window))
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), dim3(f.hkv, f.num_seqs * tiles), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), dim3(f.hkv, tiles, f.num_seqs), dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, false>), dim3(f.hq * f.num_seqs, tiles), dim3(256), 0, stream, a);
 }

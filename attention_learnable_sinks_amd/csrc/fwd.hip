@@ -77,17 +77,19 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::MIN_WG)) void fwd_kernel(FwdArg
   // BM / G query positions x the G query heads of one kv head, row r = position
   // r / G, head r % G.  A window tile then spans BM / G positions instead of BM, so
   // it visits fewer key tiles, and the G heads share each K/V tile it loads.
-  const int G = p.hq / p.hkv;
-  const XcdSlot slot = xcd_slot(blockIdx.x, p.hkv, PKH ? 1 : G);
-  const int bmq = PKH ? C::BM / G : C::BM;     // query positions per workgroup
-  // Packed: blockIdx.y = sequence x its tiles (sequence-major), so the workgroups one XCD
-  // receives are consecutive tiles of one sequence.  (Tile-major, one XCD receives one
+  // Packed: G divides BM, so it is a power of two (2^lg) and a row's position and
+  // head are a shift and a mask.  The grid is (kv head, tile, sequence): in the
+  // linear order the XCDs are dealt, kv head g lands on XCD g % 8 and each XCD
+  // receives consecutive tiles of one sequence.  (Tile-major, one XCD receives one
   // workgroup per sequence in turn; where only the longest sequence still has tiles, the
   // working workgroups recur with the period of the batch size and the ragged batch above
   // ran 23% slower than per-head tiles.)  Per-head: longest causal tiles first.
-  const int pk_tiles = PKH ? (p.max_q + bmq - 1) / bmq : 1;
-  const int b = PKH ? (int)blockIdx.y / pk_tiles : slot.seq, g = slot.kv;
-  const int tile = PKH ? (int)blockIdx.y % pk_tiles : gridDim.y - 1 - blockIdx.y;
+  const int G = p.hq / p.hkv;
+  const int lg = PKH ? __builtin_ctz(G) : 0;
+  const XcdSlot slot = PKH ? XcdSlot{(int)blockIdx.z, (int)blockIdx.x, 0} : xcd_slot(blockIdx.x, p.hkv, G);
+  const int bmq = PKH ? C::BM >> lg : C::BM;  // query positions per workgroup
+  const int b = slot.seq, g = slot.kv;
+  const int tile = PKH ? (int)blockIdx.y : gridDim.y - 1 - blockIdx.y;
 
   const SeqBounds sq = seq_bounds(p.cu_q, b, p.total_q);
   const SeqBounds sk = seq_bounds(p.cu_k, b, p.total_k);
@@ -99,13 +101,13 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::MIN_WG)) void fwd_kernel(FwdArg
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index (uniform)
   const int h = lane >> 5, c = lane & 31;
-  const int head = PKH ? g * G + (32 * w + c) % G : g * G + slot.item;  // this lane's row's head
+  const int head = PKH ? g * G + ((32 * w + c) & (G - 1)) : g * G + slot.item;  // this lane's row's head
 
   // Key range of the workgroup and of this wavefront.
   const int khi = p.causal ? clampi(qe - 1 + off + 1, 0, nk) : nk;
   const int klo = p.window > 0 ? clampi(qs + off - p.window + 1, 0, nk) : 0;
-  const int qw = PKH ? qs + (32 * w) / G : qs + 32 * w;                    // first position of the wavefront
-  const int qw_end = min(PKH ? qs + (32 * w + 31) / G + 1 : qw + 32, nq);  // one past its last
+  const int qw = PKH ? qs + ((32 * w) >> lg) : qs + 32 * w;                    // first position of the wavefront
+  const int qw_end = min(PKH ? qs + ((32 * w + 31) >> lg) + 1 : qw + 32, nq);  // one past its last
   const bool wave_rows = qw < nq;
   // Every row's keys form one interval [lo_i, hi_i) whose ends do not decrease with
   // the row: the wavefront's rows see keys in [wlo, whi) and all of them see
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::MIN_WG)) void fwd_kernel(FwdArg
   const T* vbase_p = static_cast<const T*>(p.v) + (size_t)sk.start * kv_row + g * D;
 
   // Q fragments (B operand of S^T = K Q^T): lane owns query qw + c, d = KS*s + E*h + e.
-  const int qi = PKH ? qs + (32 * w + c) / G : qw + c;  // this lane's row's position
+  const int qi = PKH ? qs + ((32 * w + c) >> lg) : qw + c;  // this lane's row's position
   typename M::Frag qf[D / KS];
   {
     const bool ok = qi < nq;
@@ -386,7 +388,7 @@ static void launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   constexpr int BM = FwdCfg<T, D>::BM;
   if (fwd_head_packed(a)) {
     const int bmq = BM / (a.hq / a.hkv);
-    dim3 grid(a.hkv, a.num_seqs * ((a.max_q + bmq - 1) / bmq));
+    dim3 grid(a.hkv, (a.max_q + bmq - 1) / bmq, a.num_seqs);
     hipLaunchKernelGGL((fwd_kernel<T, D, true>), grid, dim3(256), 0, stream, a);
   } else {
     dim3 grid(a.hq * a.num_seqs, (a.max_q + BM - 1) / BM);
