@@ -334,9 +334,18 @@ struct DkvCfg {
   static constexpr int PER_CU = (sizeof(T) == 2 && D == 64) ? 2 : 1;
 };
 
-template <typename T, int D>
+// PKH (head-packed query tiles, window layers, bf16, G = 8 query heads per kv head,
+// one head split): the 64 rows of a query tile are 8 positions x the 8 query heads
+// of the kv head (row r: position r >> 3, head r & 7), so a tile spans 8 positions
+// instead of 64.  A wavefront's 32 keys are seen by about window + 31 positions;
+// per-head 64-row tiles cover them with 3-4 tiles per head (1.2-1.6x the rows),
+// packed tiles with whole 8-position steps (about 1.05x), most of them fully
+// visible (no mask).  The rows of one position are one contiguous run of
+// 8 x D elements in Q and dO.
+template <typename T, int D, bool PKH>
 __global__ __launch_bounds__((DkvCfg<T, D>::THREADS), (sizeof(T) == 2 && D == 64) ? 2 : 1) void bwd_dkdv_kernel(
     BwdArgs a) {
+  static_assert(!PKH || sizeof(T) == 2, "head-packed dK/dV tiles are built for bf16");
   using C = DkvCfg<T, D>;
   using M = Mfma<T>;
   constexpr int E = M::E, KS = M::KS;
@@ -358,7 +367,8 @@ __global__ __launch_bounds__((DkvCfg<T, D>::THREADS), (sizeof(T) == 2 && D == 64
   const int nfold = ((f.max_k + C::BNB - 1) / C::BNB + 1) / 2;
   const bool seq_major = f.num_seqs > 1 && (int)gridDim.x == f.hkv * a.splits;
   const int b = seq_major ? (int)blockIdx.y / nfold : slot.seq, g = slot.kv, split = slot.item;
-  const int hps = (f.hq / f.hkv) / a.splits;  // query heads per split
+  const int hps = (f.hq / f.hkv) / a.splits;  // query heads per split (PKH: all 8, one split)
+  constexpr int TP = PKH ? C::BMB >> 3 : C::BMB;  // query positions per tile
   const int head0 = g * (f.hq / f.hkv) + split * hps;
 
   const SeqBounds sq = seq_bounds(f.cu_q, b, f.total_q);
@@ -390,9 +400,9 @@ __global__ __launch_bounds__((DkvCfg<T, D>::THREADS), (sizeof(T) == 2 && D == 64
     const int kend = min(kbase + C::BNB, nk);
     const int qlo = f.causal ? clampi(kbase - off, 0, nq) : 0;
     const int qhi = f.window > 0 ? clampi(kend - 1 - off + f.window, 0, nq) : nq;
-    const int qt_begin = qlo / C::BMB;
-    const int nqt = qhi > qlo ? (qhi + C::BMB - 1) / C::BMB - qt_begin : 0;
-    const int n_it = hps * nqt;
+    const int qt_begin = qlo / TP;
+    const int nqt = qhi > qlo ? (qhi + TP - 1) / TP - qt_begin : 0;
+    const int n_it = PKH ? nqt : hps * nqt;
 
     const int kw = kbase + 32 * w;
     const int kw_end = min(kw + 32, nk);
@@ -428,8 +438,28 @@ __global__ __launch_bounds__((DkvCfg<T, D>::THREADS), (sizeof(T) == 2 && D == 64
     QLoader qld, dold;
     RowLoader lld, dld;  // the tile's lse * log2(e) and -D rows (waves 0 and 1)
     int staged_head = -1;
+    if constexpr (PKH) {
+      // One set of descriptors for the whole loop.  The row statistics of head
+      // head0 + j sit 2 total_q apart; rows past the sequence read the next
+      // sequence's (finite) statistics or zero past the array, and only ever meet
+      // masked (zero) probabilities.
+      qld.init_rows(qhead_p + head0 * D, q_row, nq, tid, 3, D * sizeof(T));
+      dold.init_rows(dohead_p + head0 * D, q_row, nq, tid, 3, D * sizeof(T));
+      const long long stat0 = (long long)(2 * head0) * f.total_q + sq.start;
+      const int nstat = (int)((long long)2 * f.hq * f.total_q - stat0);
+      lld.init_packed(a.rowstat + stat0, nstat);
+      dld.init_packed(a.rowstat + stat0 + f.total_q, nstat - f.total_q);
+    }
     // Start moving (head, query tile) of iteration `it` into LDS buffer `buf`.
     auto stage = [&](int it, int buf) __device__ {
+      if constexpr (PKH) {
+        const int qt = qt_begin + it;
+        qld.issue(qt * TP, smem + buf * 2 * C::TILE);
+        dold.issue(qt * TP, smem + buf * 2 * C::TILE + C::TILE);
+        if (w == 0) lld.issue_packed(qt * TP, nlse_s[buf], lane, 3, 2 * f.total_q);
+        if (w == 1) dld.issue_packed(qt * TP, dd_s[buf], lane, 3, 2 * f.total_q);
+        return;
+      }
       const int hd = head0 + it / nqt;
       const int qt = qt_begin + it % nqt;
       if (hd != staged_head) {  // uniform: new descriptors when the query head changes
@@ -508,8 +538,10 @@ __global__ __launch_bounds__((DkvCfg<T, D>::THREADS), (sizeof(T) == 2 && D == 64
             const int r = 4 * r4 + e;
             float pv = fast_exp2(fmaf(pt[mq][r], sl2, l4[e]));  // nlse_s holds -lse * log2(e)
             if constexpr (!FULL) {
-              // query qbase + 4h + (32 mq + 8 r4 + e), a constant per element
-              pv = in_span(qbase + 4 * h + 32 * mq + 8 * r4 + e, key_rows) ? pv : 0.f;
+              // tile row 4h + 32 mq + 8 r4 + e: per-head tiles, query qbase + that row;
+              // packed, position qbase + 4 mq + r4 (the row >> 3), a constant per element
+              const int qrow = PKH ? qbase + 4 * mq + r4 : qbase + 4 * h + 32 * mq + 8 * r4 + e;
+              pv = in_span(qrow, key_rows) ? pv : 0.f;
             }
             pt[mq][r] = pv;
             dst[mq][r] = pv * dst[mq][r];  // dS = P (dP - D)
@@ -536,11 +568,11 @@ __global__ __launch_bounds__((DkvCfg<T, D>::THREADS), (sizeof(T) == 2 && D == 64
       // bf16: tile it+2 goes to the buffer read in the previous step; fp32: tile it+1.
       const bool more = it + NB - 1 < n_it;
       if (more) stage(it + NB - 1, (it + NB - 1) % NB);
-      const int qbase = qt * C::BMB;
+      const int qbase = qt * TP;  // first query position of the tile
       if constexpr (FULL) {
         body(buf, qbase, full_tag);
       } else {
-        const int qlast = min(qbase + C::BMB, nq) - 1;
+        const int qlast = min(qbase + TP, nq) - 1;
         if (wave_keys && qbase < wqhi && qlast >= wqlo) body(buf, qbase, full_tag);
       }
       if constexpr (NB == 3) {
@@ -567,11 +599,11 @@ __global__ __launch_bounds__((DkvCfg<T, D>::THREADS), (sizeof(T) == 2 && D == 64
     if (kw + 32 <= nk) {
       const int lo_q = f.causal ? kw + 31 - off : 0;                      // first row seeing all 32 keys
       const int hi_q = f.window > 0 ? min(kw - off + f.window, nq) : nq;  // rows below this see them too
-      qf_lo = clampi(lo_q > 0 ? (lo_q + C::BMB - 1) / C::BMB : 0, qt_begin, qt_end);
-      qf_hi = clampi(hi_q > 0 ? hi_q / C::BMB : 0, qf_lo, qt_end);
+      qf_lo = clampi(lo_q > 0 ? (lo_q + TP - 1) / TP : 0, qt_begin, qt_end);
+      qf_hi = clampi(hi_q > 0 ? hi_q / TP : 0, qf_lo, qt_end);
     }
     int it = 0;
-    for (int hd = 0; hd < hps; ++hd) {
+    for (int hd = 0; hd < (PKH ? 1 : hps); ++hd) {
       int qt = qt_begin;
       for (; qt < qf_lo; ++qt, ++it) step(it, qt, std::false_type{});
       for (; qt < qf_hi; ++qt, ++it) step(it, qt, std::true_type{});
@@ -695,16 +727,21 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int fp32, hipStream_t stream) {
                     : dim3(a.f.hkv * a.splits * a.f.num_seqs, nfold);
     hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, stream, a);
   };
-  if (a.f.d == 128) {
-    if (fp32)
-      launch(bwd_dkdv_kernel<float, 128>, DkvCfg<float, 128>::BNB, DkvCfg<float, 128>::THREADS);
+  if (!fp32 && dkdv_head_packed(a.f.hq, a.f.hkv, a.f.window, a.splits)) {
+    if (a.f.d == 128)
+      launch(bwd_dkdv_kernel<bf16, 128, true>, DkvCfg<bf16, 128>::BNB, DkvCfg<bf16, 128>::THREADS);
     else
-      launch(bwd_dkdv_kernel<bf16, 128>, DkvCfg<bf16, 128>::BNB, DkvCfg<bf16, 128>::THREADS);
+      launch(bwd_dkdv_kernel<bf16, 64, true>, DkvCfg<bf16, 64>::BNB, DkvCfg<bf16, 64>::THREADS);
+  } else if (a.f.d == 128) {
+    if (fp32)
+      launch(bwd_dkdv_kernel<float, 128, false>, DkvCfg<float, 128>::BNB, DkvCfg<float, 128>::THREADS);
+    else
+      launch(bwd_dkdv_kernel<bf16, 128, false>, DkvCfg<bf16, 128>::BNB, DkvCfg<bf16, 128>::THREADS);
   } else {
     if (fp32)
-      launch(bwd_dkdv_kernel<float, 64>, DkvCfg<float, 64>::BNB, DkvCfg<float, 64>::THREADS);
+      launch(bwd_dkdv_kernel<float, 64, false>, DkvCfg<float, 64>::BNB, DkvCfg<float, 64>::THREADS);
     else
-      launch(bwd_dkdv_kernel<bf16, 64>, DkvCfg<bf16, 64>::BNB, DkvCfg<bf16, 64>::THREADS);
+      launch(bwd_dkdv_kernel<bf16, 64, false>, DkvCfg<bf16, 64>::BNB, DkvCfg<bf16, 64>::THREADS);
   }
   return hipGetLastError();
 }

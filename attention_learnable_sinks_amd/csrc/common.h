@@ -407,7 +407,14 @@ struct TileLoader<bf16, ROWS, THREADS> {
   uint32_t row_bytes;
   uint32_t voff[N];
   int first_slot;  // first LDS slot (of 64) written by this wavefront's instructions
+  // Tile row r is array row row0 + r.
   __device__ inline void init(const bf16* base, size_t row_stride, int nrows, int tid) {
+    init_rows(base, row_stride, nrows, tid, 0, 0u);
+  }
+  // Packed rows: tile row r is array row row0 + (r >> lg), plus (r & (2^lg - 1)) *
+  // sub_bytes within it (the heads of one position); rows >= nrows read as zero.
+  __device__ inline void init_rows(const bf16* base, size_t row_stride, int nrows, int tid, int lg,
+                                   uint32_t sub_bytes) {
     base_ = base;
     nrows_ = nrows;
     row_bytes = (uint32_t)(row_stride * sizeof(bf16));
@@ -419,7 +426,8 @@ struct TileLoader<bf16, ROWS, THREADS> {
       const int slot = first_slot + n * 64 + lane;  // LDS byte offset 16 * slot in the tile
       const int r = slot >> 3, pc = slot & 7;
       const int col_chunk = pc ^ Tile<bf16>::swz(r);  // slot (r, pc) holds logical chunk pc ^ swz(r)
-      voff[n] = (uint32_t)r * row_bytes + (uint32_t)col_chunk * 16u;
+      voff[n] = (uint32_t)(r >> lg) * row_bytes + (uint32_t)(r & ((1 << lg) - 1)) * sub_bytes +
+                (uint32_t)col_chunk * 16u;
     }
   }
   __device__ inline void issue(int row0, bf16* tile) {
@@ -470,6 +478,11 @@ struct TileLoaderD {
 #pragma unroll
     for (int i = 0; i < BLOCKS; ++i) sub[i].init(base + kD * i, row_stride, nrows, tid);
   }
+  // Packed rows (bf16 only): see TileLoader<bf16>::init_rows.
+  __device__ inline void init_rows(const T* base, size_t row_stride, int nrows, int tid, int lg, uint32_t sub_bytes) {
+#pragma unroll
+    for (int i = 0; i < BLOCKS; ++i) sub[i].init_rows(base + kD * i, row_stride, nrows, tid, lg, sub_bytes);
+  }
   __device__ inline void issue(int row0, T* tile) {
 #pragma unroll
     for (int i = 0; i < BLOCKS; ++i) sub[i].issue(row0, tile + i * tile_elems<T>(ROWS));
@@ -493,6 +506,15 @@ struct RowLoader {
   __device__ inline void issue(int row0, float* lds, int lane) {
 #if defined(__HIP_DEVICE_COMPILE__)
     lds_dma_b32(rsrc, (uint32_t)(row0 + lane) * 4u, lds_address(lds));
+#endif
+  }
+  // Packed rows: lane i takes element row0 + (i >> lg) of sub-array i & (2^lg - 1),
+  // the sub-arrays `sub_stride` floats apart (readable range: `nvals` floats).
+  __device__ inline void init_packed(const float* base, int nvals) { rsrc = rows_rsrc(base, (uint32_t)nvals * 4u); }
+  __device__ inline void issue_packed(int row0, float* lds, int lane, int lg, int sub_stride) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint32_t i = (uint32_t)(lane & ((1 << lg) - 1)) * (uint32_t)sub_stride + (uint32_t)(row0 + (lane >> lg));
+    lds_dma_b32(rsrc, i * 4u, lds_address(lds));
 #endif
   }
 };

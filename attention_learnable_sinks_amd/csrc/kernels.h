@@ -78,6 +78,10 @@ constexpr int kDecodeChunk = 32;  // key tiles per decoding chunk (1024 keys)
 
 // Head-packed dQ tiles (window layers) and dQ row tiles per sequence.
 bool dq_head_packed(int hq, int hkv, int num_seqs, int max_q, int window);
+// Head-packed dK/dV query tiles (window layers, bf16, 8 query heads per kv head, one split).
+inline bool dkdv_head_packed(int hq, int hkv, int window, int splits) {
+  return window > 0 && splits == 1 && hkv > 0 && hq == 8 * hkv;
+}
 int dq_tiles(int hq, int hkv, int num_seqs, int max_q, int window);
 
 // Workspace layout for a backward call; offsets in bytes from the workspace base.

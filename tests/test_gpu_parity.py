@@ -43,6 +43,7 @@ SMALL = [
     ([190, 450], 4, 4, False, 100, ("uniform", -2.0, 8.0)),
     ([513], 16, 2, True, 128, ("normal",)),
     ([300], 16, 1, True, 0, ("normal",)),  # one kv head: dK/dV over 16 head splits
+    ([200, 77, 345], 16, 2, True, 50, ("uniform", -2.0, 8.0)),  # 8 heads per kv head: packed window tiles
 ]
 
 
@@ -194,9 +195,12 @@ def test_head_packed_tiles_bitwise(gpu_lib, dtype, hq, hkv, causal):
     head (rows = positions x heads); layers without a window run on per-head tiles.
     A row's arithmetic depends only on its own scores, with key tiles at the same
     absolute key positions, so (1) a window of at least n keys (packed) gives
-    bitwise the per-head causal / full O, LSE, dQ, dK and dV, and dS_h up to the
-    rounding order of its partials, and (2) a sequence alone gives bitwise the rows
-    it gets inside a ragged batch."""
+    bitwise the per-head causal / full O, LSE and dQ, and dS_h up to the rounding
+    order of its partials, and (2) a sequence alone gives bitwise the rows it gets
+    inside a ragged batch.  dK and dV sum over (head, row); with 8 query heads per kv
+    head the bf16 window backward packs its query tiles too, which changes that
+    order, so there they agree to one rounding of the element type (bitwise
+    otherwise)."""
     n, m, window = 300, 77, 70
     inp = random_case([n, m], hq, hkv, 64, dtype, seed=hq + hkv + int(causal), causal=causal, window=window)
     d = to_dev(inp)
@@ -214,8 +218,14 @@ def test_head_packed_tiles_bitwise(gpu_lib, dtype, hq, hkv, causal):
     o1, lse1 = gpu_lib.fwd(q, k, v, d["sinks"], cu1, cu1, n, n, sc, causal, window)
     torch.cuda.synchronize()
     assert torch.equal(o_wide, o_none) and torch.equal(lse_wide, lse_none)
-    for name, x, y in zip(("dq", "dk", "dv"), g_wide[:3], g_none[:3]):
-        assert torch.equal(x, y), name
+    assert torch.equal(g_wide[0], g_none[0]), "dq"
+    for name, x, y in zip(("dk", "dv"), g_wide[1:3], g_none[1:3]):
+        if dtype == "bf16" and hq == 8 * hkv:
+            ymax = y.float().abs().max().item()
+            ulp = 2.0 ** (np.floor(np.log2(ymax)) - 7)  # one bf16 ulp at the tensor's largest magnitude
+            assert (x.float() - y.float()).abs().max().item() <= ulp, name
+        else:
+            assert torch.equal(x, y), name
     # dS_h partials group the rows per packed tile: the same sum up to rounding order
     torch.testing.assert_close(g_wide[3], g_none[3], rtol=1e-5, atol=1e-7)
     assert torch.equal(o1, o2[:n]) and torch.equal(lse1, lse2[:, :n])
