@@ -25,6 +25,7 @@ CASES = [
     ([257], 4, 2, False, 0),
     ([190, 450], 4, 4, False, 100),
     ([300], 8, 2, True, 64),  # one sequence, window: head-packed forward tiles
+    ([200, 77, 345], 16, 2, True, 50),  # 8 query heads per kv head, window: packed dK/dV tiles too
 ]
 
 
