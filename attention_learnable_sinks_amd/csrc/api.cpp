@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <initializer_list>
@@ -30,13 +31,15 @@ const char* kernel_name(int id) {
 
 namespace {
 
-// ---- opt-in timing records
+// ---- opt-in timing records: the library's only mutable host state.  With timing
+// off (the default) a launch reads the flag and nothing else; with it on, each
+// launch appends one event pair under the mutex.
 struct Record {
   int kernel;
   hipEvent_t start, stop;
 };
-std::mutex g_mu;
-bool g_timing = false;
+std::mutex g_mu;  // guards g_records
+std::atomic<bool> g_timing{false};
 std::vector<Record> g_records;
 
 void clear_records_locked() {
@@ -49,11 +52,7 @@ void clear_records_locked() {
 
 template <typename F>
 attn_sink_status timed_launch(int kernel, hipStream_t stream, F&& launch) {
-  bool timing;
-  {
-    std::lock_guard<std::mutex> lk(g_mu);
-    timing = g_timing;
-  }
+  const bool timing = g_timing.load(std::memory_order_acquire);
   Record rec{kernel, nullptr, nullptr};
   // Events of a failed launch are released here (a recorded event may be destroyed
   // before it completes; the runtime frees it once it has).
@@ -327,7 +326,7 @@ const char* attn_sink_status_string(attn_sink_status status) {
 attn_sink_status attn_sink_timing_enable(int enable) {
   std::lock_guard<std::mutex> lk(g_mu);
   if (enable) clear_records_locked();
-  g_timing = enable != 0;
+  g_timing.store(enable != 0, std::memory_order_release);
   return ATTN_SINK_OK;
 }
 
