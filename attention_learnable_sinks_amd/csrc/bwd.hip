@@ -450,6 +450,9 @@ __global__ __launch_bounds__((DkvCfg<T, D>::THREADS), (sizeof(T) == 2 && D == 64
       lld.init_packed(a.rowstat + stat0, nstat);
       dld.init_packed(a.rowstat + stat0 + f.total_q, nstat - f.total_q);
     }
+    // The next (head, query tile) to stage: stage() is called for iterations 0, 1, 2, ...
+    // in order, so it advances a counter instead of dividing the iteration index.
+    int st_hd = head0, st_qt = qt_begin;
     // Start moving (head, query tile) of iteration `it` into LDS buffer `buf`.
     auto stage = [&](int it, int buf) __device__ {
       if constexpr (PKH) {
@@ -460,8 +463,11 @@ __global__ __launch_bounds__((DkvCfg<T, D>::THREADS), (sizeof(T) == 2 && D == 64
         if (w == 1) dld.issue_packed(qt * TP, dd_s[buf], lane, 3, 2 * f.total_q);
         return;
       }
-      const int hd = head0 + it / nqt;
-      const int qt = qt_begin + it % nqt;
+      const int hd = st_hd, qt = st_qt;
+      if (++st_qt == qt_begin + nqt) {
+        st_qt = qt_begin;
+        ++st_hd;
+      }
       if (hd != staged_head) {  // uniform: new descriptors when the query head changes
         qld.init(qhead_p + hd * D, q_row, nq, tid);
         dold.init(dohead_p + hd * D, q_row, nq, tid);
