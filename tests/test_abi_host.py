@@ -336,3 +336,20 @@ def test_noalloc_decode_refuses_shapes_beyond_its_scratch(lib):
     for kw, status in BAD_SHAPES:  # the shape checks come first, as in attn_sink_fwd_decode
         s = _decode_shape(**kw)
         assert lib.attn_sink_fwd_decode_noalloc(ctypes.byref(s), *[FAKE] * 6, None) == status, kw
+
+
+def test_thirty_two_bit_offset_bound(lib):
+    """A kernel reads one head of one sequence through a buffer descriptor with 32-bit
+    byte offsets, and a tile may start on the last row, so (max_seqlen + 128) x row
+    pitch must stay below 2^32: Hq = 64, d = 64, bf16 (pitch 8192 B) allows 524159
+    query rows, Hkv = 8 (pitch 1024 B) 4194175 key rows; one more is refused."""
+    def ws(max_q, max_k):
+        s = _shape(num_heads_q=64, num_heads_kv=8, total_q=max_q, total_k=max_k, max_seqlen_q=max_q,
+                   max_seqlen_k=max_k)
+        return lib.attn_sink_bwd_workspace_bytes(ctypes.byref(s))
+    assert ((524159 + 128) * 8192) < 2 ** 32 <= ((524160 + 128) * 8192)
+    assert ((4194175 + 128) * 1024) < 2 ** 32 <= ((4194176 + 128) * 1024)
+    assert ws(524159, 128) > 0 and ws(524160, 128) == 0
+    assert ws(128, 4194175) > 0 and ws(128, 4194176) == 0
+    s = _shape(num_heads_q=64, num_heads_kv=8, total_q=524160, max_seqlen_q=524160)
+    assert lib.attn_sink_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == als.ERR_UNSUPPORTED
