@@ -226,8 +226,17 @@ def test_head_packed_tiles_bitwise(gpu_lib, dtype, hq, hkv, causal):
             assert (x.float() - y.float()).abs().max().item() <= ulp, name
         else:
             assert torch.equal(x, y), name
-    # dS_h partials group the rows per packed tile: the same sum up to rounding order
-    torch.testing.assert_close(g_wide[3], g_none[3], rtol=1e-5, atol=1e-7)
+    # dS_h = -sum_i P_sink,i D_i over the head's rows; packed tiles group those rows
+    # into other partials, so the two agree up to the order of a float32 sum of n
+    # terms.  Either order lies within (n-1) u sum_i |P_sink,i D_i| of the exact sum
+    # (u = 2^-24), so the two within twice that.  The terms cancel, so the bar is set
+    # by their absolute sum, not by |dS_h|.
+    o64 = o_none.double().cpu()
+    dd = (o64 * do.double().cpu()).sum(-1)  # D_i = dO_i . O_i, [n, hq]
+    psink = torch.exp(d["sinks"].double().cpu()[None, :] - lse_none.double().cpu().T)  # [n, hq]
+    bound = 2 * (n - 1) * 2.0**-24 * (psink * dd).abs().sum(0)
+    diff = (g_wide[3].double() - g_none[3].double()).abs().cpu()
+    assert bool((diff <= bound).all()), f"dS_h {diff.tolist()} vs {bound.tolist()}"
     assert torch.equal(o1, o2[:n]) and torch.equal(lse1, lse2[:, :n])
     ref = oracle_bwd(inp)
     compare({"o": o2.float().cpu().numpy().astype(np.float64), "lse": lse2.cpu().numpy().astype(np.float64)},
