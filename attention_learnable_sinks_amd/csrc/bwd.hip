@@ -181,56 +181,89 @@ __global__ __launch_bounds__(256, (DqCfg<T, D>::MIN_WG)) void bwd_dq_kernel(BwdA
         masked |= (k >= wlo_all && k + 32 <= whi_all) ? 0 : 1 << mt;
       }
     }
-    f32x16 st[2], dpt[2];  // S^T, dP^T: [64 keys x 32 q]
-    // Issue priority while this wavefront feeds the matrix cores, so the other
-    // wavefronts on the SIMD fill the vector ALUs meanwhile (measured faster here).
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    // S^T, dP^T of the 32 keys kbase + 32 mt ..+32 against the wavefront's 32 rows.
+    auto scores = [&](int mt, f32x16& st_out, f32x16& dpt_out) {
+      f32x16 st, dpt;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        st[mt][r] = 0.f;
-        dpt[mt][r] = 0.f;
+        st[r] = 0.f;
+        dpt[r] = 0.f;
       }
 #pragma unroll
       for (int s = 0; s < D / KS; ++s) {
-        st[mt] = M::mma(frag_row<T, C::BN>(fa, Ks, mt, s), qf[s], st[mt]);
+        st = M::mma(frag_row<T, C::BN>(fa, Ks, mt, s), qf[s], st);
         const auto vfr = frag_row<T, C::BN>(fa, Vs, mt, s);
         if constexpr (sizeof(T) == 2) {
           // bf16: dP^T starts from -D (a loop-invariant seed), so it ends at dP^T - D.
-          dpt[mt] = s == 0 ? mma_seeded(vfr, dof[s], neg_dd) : M::mma(vfr, dof[s], dpt[mt]);
+          dpt = s == 0 ? mma_seeded(vfr, dof[s], neg_dd) : M::mma(vfr, dof[s], dpt);
         } else {
-          dpt[mt] = M::mma(vfr, dof[s], dpt[mt]);
+          dpt = M::mma(vfr, dof[s], dpt);
         }
       }
-    }
-    __builtin_amdgcn_s_setprio(0);
-    float tsum[2];  // the tile's row sums of dS^T, one chain per 32 keys
+      st_out = st;
+      dpt_out = dpt;
+    };
+    // S^T -> P^T -> dS^T = P^T (dP^T - D) in place; returns the half's sum of dS^T.
+    auto grads = [&](int mt, f32x16& st, const f32x16& dpt) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[mt][r] = fast_exp2(fmaf(st[mt][r], sl2, -lse2));  // P^T
+      for (int r = 0; r < 16; ++r) st[r] = fast_exp2(fmaf(st[r], sl2, -lse2));  // P^T
       if (!FULL && (masked >> mt & 1)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)  // key kbase + 4h + (32 mt + 8 (r/4) + r%4)
-          st[mt][r] = in_span(kbase + 4 * h + 32 * mt + 8 * (r / 4) + r % 4, row_keys) ? st[mt][r] : 0.f;
+          st[r] = in_span(kbase + 4 * h + 32 * mt + 8 * (r / 4) + r % 4, row_keys) ? st[r] : 0.f;
       }
+      float t = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        st[mt][r] *= sizeof(T) == 2 ? dpt[mt][r] : dpt[mt][r] - dd;  // dS^T = P^T (dP^T - D)
-        tsum[mt] = r == 0 ? st[mt][r] : tsum[mt] + st[mt][r];
+        st[r] *= sizeof(T) == 2 ? dpt[r] : dpt[r] - dd;
+        t = r == 0 ? st[r] : t + st[r];
       }
+      return t;
+    };
+    // dQ^T[d x q] += K^T[d x keys] . dS^T[keys x q] over contraction steps s0 ..+ns of
+    // the tile, with dS^T held from step s0 on in st.
+    auto dq_update = [&](const f32x16* st, int s0, auto ns_tag) {
+      constexpr int NS = decltype(ns_tag)::value;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const typename M::Frag sf = pack_frag<T>(st, s);
+#pragma unroll
+        for (int md = 0; md < D / 32; ++md)
+          dqt[md] = M::mma(frag_col<T, C::BN>(fa, Ks, md, s0 + s), sf, dqt[md]);
+      }
+    };
+    constexpr int NS = C::BN / KS;  // dQ contraction steps per tile
+    // Issue priority is raised while this wavefront feeds the matrix cores, so the
+    // other wavefronts on the SIMD fill the vector ALUs meanwhile (measured faster).
+    float tsum[2];  // the tile's row sums of dS^T, one chain per 32 keys
+    if constexpr (D == 64) {
+      // One 32-key half at a time: only one half's scores are live, which keeps
+      // the kernel at its register cap without spills.  Same products, same order.
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        f32x16 st, dpt;
+        __builtin_amdgcn_s_setprio(1);
+        scores(mt, st, dpt);
+        __builtin_amdgcn_s_setprio(0);
+        tsum[mt] = grads(mt, st, dpt);
+        __builtin_amdgcn_s_setprio(1);
+        dq_update(&st, mt * (NS / 2), std::integral_constant<int, NS / 2>{});
+        __builtin_amdgcn_s_setprio(0);
+      }
+    } else {
+      // Both halves' scores first: at D = 128 this schedules better than by halves.
+      f32x16 st[2], dpt[2];
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) scores(mt, st[mt], dpt[mt]);
+      __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) tsum[mt] = grads(mt, st[mt], dpt[mt]);
+      __builtin_amdgcn_s_setprio(1);
+      dq_update(st, 0, std::integral_constant<int, NS>{});
+      __builtin_amdgcn_s_setprio(0);
     }
     dsum += tsum[0] + tsum[1];
-    // dQ^T[d x q] += K^T[d x keys] . dS^T[keys x q]
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int s = 0; s < C::BN / KS; ++s) {
-      const typename M::Frag sf = pack_frag<T>(st, s);
-#pragma unroll
-      for (int md = 0; md < D / 32; ++md) dqt[md] = M::mma(frag_col<T, C::BN>(fa, Ks, md, s), sf, dqt[md]);
-    }
-    __builtin_amdgcn_s_setprio(0);
   };
   auto step = [&](int kt, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
