@@ -251,7 +251,8 @@ __global__ __launch_bounds__(256, (DqCfg<T, D>::MIN_WG)) void bwd_dq_kernel(BwdA
         __builtin_amdgcn_s_setprio(0);
       }
     } else {
-      // Both halves' scores first: at D = 128 this schedules better than by halves.
+      // Both halves' scores first: at D = 128 the by-halves form spills (bf16) or needs
+      // more registers (fp32, 471 against 395).
       f32x16 st[2], dpt[2];
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
