@@ -22,7 +22,9 @@
 //                  once, scaled, in the element type.
 //   2. bwd_dkdv:   key-stationary: a workgroup owns 128 keys of one kv head (32 per
 //                  wavefront, K and V in registers) and loops over the query heads of
-//                  its share of the GQA group and over the query tiles of the band:
+//                  its share of the GQA group and over the query tiles of the band
+//                  (per-head tiles from the last down, so that the workgroups sharing
+//                  a head's Q and dO read the same rows together):
 //                  S = Q K^T, dP = dO V^T put the key on the lane, so P and dS feed
 //                  dV^T += dO^T P and dK^T += Q^T dS from registers, with dO^T and Q^T
 //                  read transposed from row-major LDS tiles.  Under a causal mask key
@@ -486,7 +488,14 @@ __global__ __launch_bounds__((DkvCfg<T, D>::THREADS), (sizeof(T) == 2 && D == 64
     }
     // The next (head, query tile) to stage: stage() is called for iterations 0, 1, 2, ...
     // in order, so it advances a counter instead of dividing the iteration index.
-    int st_hd = head0, st_qt = qt_begin;
+    // Per-head tiles walk the query tiles from the last down.  Causal key tiles all see
+    // the rows from their own up to the end of the sequence, so the workgroups that
+    // share a head's Q and dO then read the same rows at about the same time, and the
+    // L2 serves the re-reads.  (Packed tiles only run window layers, whose ranges
+    // overlap between neighbouring key tiles alone; they walk upwards.)
+    constexpr bool DOWN = !PKH;
+    const int qt_first = DOWN ? qt_begin + nqt - 1 : qt_begin;
+    int st_hd = head0, st_qt = qt_first;
     // Start moving (head, query tile) of iteration `it` into LDS buffer `buf`.
     auto stage = [&](int it, int buf) __device__ {
       if constexpr (PKH) {
@@ -498,8 +507,8 @@ __global__ __launch_bounds__((DkvCfg<T, D>::THREADS), (sizeof(T) == 2 && D == 64
         return;
       }
       const int hd = st_hd, qt = st_qt;
-      if (++st_qt == qt_begin + nqt) {
-        st_qt = qt_begin;
+      if (DOWN ? --st_qt < qt_begin : ++st_qt == qt_begin + nqt) {
+        st_qt = qt_first;
         ++st_hd;
       }
       if (hd != staged_head) {  // uniform: new descriptors when the query head changes
@@ -644,10 +653,17 @@ __global__ __launch_bounds__((DkvCfg<T, D>::THREADS), (sizeof(T) == 2 && D == 64
     }
     int it = 0;
     for (int hd = 0; hd < (PKH ? 1 : hps); ++hd) {
-      int qt = qt_begin;
-      for (; qt < qf_lo; ++qt, ++it) step(it, qt, std::false_type{});
-      for (; qt < qf_hi; ++qt, ++it) step(it, qt, std::true_type{});
-      for (; qt < qt_end; ++qt, ++it) step(it, qt, std::false_type{});
+      if constexpr (DOWN) {
+        int qt = qt_end - 1;
+        for (; qt >= qf_hi; --qt, ++it) step(it, qt, std::false_type{});
+        for (; qt >= qf_lo; --qt, ++it) step(it, qt, std::true_type{});
+        for (; qt >= qt_begin; --qt, ++it) step(it, qt, std::false_type{});
+      } else {
+        int qt = qt_begin;
+        for (; qt < qf_lo; ++qt, ++it) step(it, qt, std::false_type{});
+        for (; qt < qf_hi; ++qt, ++it) step(it, qt, std::true_type{});
+        for (; qt < qt_end; ++qt, ++it) step(it, qt, std::false_type{});
+      }
     }
 
     // Lane owns key kj; register r of tile md holds d = 32 md + crow(r, h).
