@@ -44,6 +44,8 @@ SMALL = [
     ([513], 16, 2, True, 128, ("normal",)),
     ([300], 16, 1, True, 0, ("normal",)),  # one kv head: dK/dV over 16 head splits
     ([200, 77, 345], 16, 2, True, 50, ("uniform", -2.0, 8.0)),  # 8 heads per kv head: packed window tiles
+    ([300, 45], 16, 2, True, 1, ("uniform", -2.0, 8.0)),  # window 1: every row sees its own key only
+    ([260, 3], 4, 2, True, 65, ("normal",)),  # window one key past a 64-key tile
 ]
 
 

@@ -194,6 +194,34 @@ def test_single_key_row():
     np.testing.assert_allclose(lse[0, 0], np.logaddexp(s00, sink[0]), atol=1e-14)
 
 
+def test_window_one_is_a_single_key_per_row():
+    """Window 1 (causal): every row sees its own key only, so with p_i = sigmoid(s_ii - S_h)
+    the forward is O_i = p_i v_i, LSE_i = logaddexp(s_ii, S_h), and the chain rule through
+    the two-entry softmax [s_ii, S_h] gives dS_ii = p_i (1 - p_i) <dO_i, v_i>,
+    dq_i = scale dS_ii k_i, dk_i = scale sum_h dS_ii q_i (over the kv head's query heads),
+    dv_i = sum_h p_i dO_i and dS_h = -sum_i (1 - p_i) p_i <dO_i, v_i>."""
+    rng = np.random.default_rng(17)
+    lens, hq, hkv, d, scale = [5, 3], 4, 2, 6, 0.4
+    n, g = sum(lens), hq // hkv
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k, v, do = _rand(rng, n, hq, d), _rand(rng, n, hkv, d), _rand(rng, n, hkv, d), _rand(rng, n, hq, d)
+    sinks = rng.standard_normal(hq)
+    r = _bwd(q, k, v, sinks, do, cu, scale, True, 1)
+    kh, vh = np.repeat(k, g, axis=1), np.repeat(v, g, axis=1)  # [n, hq, d]
+    s = scale * np.einsum("nhd,nhd->nh", q, kh)
+    p = 1.0 / (1.0 + np.exp(sinks[None, :] - s))
+    dp = np.einsum("nhd,nhd->nh", do, vh)
+    ds = p * (1 - p) * dp
+    np.testing.assert_allclose(r["o"], p[..., None] * vh, atol=1e-13)
+    np.testing.assert_allclose(r["lse"], np.logaddexp(s, sinks[None, :]).T, atol=1e-13)
+    np.testing.assert_allclose(r["dq"], scale * ds[..., None] * kh, atol=1e-13)
+    dk = (scale * ds[..., None] * q).reshape(n, hkv, g, d).sum(2)
+    dv = (p[..., None] * do).reshape(n, hkv, g, d).sum(2)
+    np.testing.assert_allclose(r["dk"], dk, atol=1e-13)
+    np.testing.assert_allclose(r["dv"], dv, atol=1e-13)
+    np.testing.assert_allclose(r["dsinks"], -((1 - p) * p * dp).sum(0), atol=1e-13)
+
+
 def test_empty_row_and_empty_sequence():
     """A sequence of length 0 writes nothing; a row with no visible key (N_q > N_k,
     causal) has O = 0 and LSE = S_h; with S_h = -inf it has LSE = -inf."""
