@@ -57,6 +57,10 @@
  *
  * Thread safety: calls are reentrant; concurrent calls on different streams are
  * independent (they must not share output or workspace buffers).
+ *
+ * Graph capture: no entry point allocates, sets memory or synchronises, so every
+ * call can be captured into a HIP graph on `stream` (with the timing records off);
+ * each replay overwrites every output, so it depends on its inputs alone.
  */
 #ifndef ATTN_SINK_H
 #define ATTN_SINK_H
