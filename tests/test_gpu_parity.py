@@ -46,6 +46,7 @@ SMALL = [
     ([200, 77, 345], 16, 2, True, 50, ("uniform", -2.0, 8.0)),  # 8 heads per kv head: packed window tiles
     ([300, 45], 16, 2, True, 1, ("uniform", -2.0, 8.0)),  # window 1: every row sees its own key only
     ([260, 3], 4, 2, True, 65, ("normal",)),  # window one key past a 64-key tile
+    ([300, 45], 16, 2, False, 60, ("uniform", -2.0, 8.0)),  # packed tiles, window without causal mask
 ]
 
 
