@@ -424,7 +424,9 @@ def main():
                 "bwd_ms": round(sum(v for k, v in per_c.items() if k != "attn_sink_fwd_kernel"), 5),
                 "steps": args.cold_steps}
 
-    fig, fwd_flop, bwd_flop = figures(w, step, per, args.workload)
+    # committed profiles are named per layer for workloads with several layer calls
+    wname = f"{args.workload}_layer{args.layer}" if len(w.layers) > 1 else args.workload
+    fig, fwd_flop, bwd_flop = figures(w, step, per, wname)
     ms = (t1 - t0) * 1e3 / args.steps
     value = (fwd_flop + bwd_flop) / (ms * 1e-3) / 1e12
     roofline = fig["roofline"]
@@ -432,7 +434,7 @@ def main():
     # The same against the clock the kernel actually ran at (CUs x 4096 bf16 FLOP per clock x
     # the core clock from the committed counter run, an upper bound, so this fraction is a
     # lower bound).
-    sclk = read_sclk(args.workload, dom) if roofline["bound"] == "mfma" and w.dtype == "bf16" else None
+    sclk = read_sclk(wname, dom) if roofline["bound"] == "mfma" and w.dtype == "bf16" else None
     if sclk is not None:
         cus = torch.cuda.get_device_properties(dev).multi_processor_count
         adj = cus * 4096 * sclk * 1e9 / 1e12
